@@ -1,0 +1,241 @@
+"""Benchmark: split-KV paged decode on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config gqa_64k] [--splits S]
+
+One step = one decode op (stage 1 + stage 2) over one batch of the workload.
+Inputs are seeded synthetic data resident in HBM before timing starts.  The
+KV pool is replicated R times and step i reads replica i mod R, so every step
+reads KV that no cache still holds (R x touched bytes >= 1 GiB, four times the
+last-level cache).  The K timed steps run as one captured HIP graph
+(launch overhead excluded) bracketed by torch.cuda.synchronize(); HIP events
+on the launch stream give the time.  Stage 1 alone is timed the same way
+(a graph of K stage-1 launches) for the roofline entry.
+
+Prints one JSON line.  value = logical KV bytes per op / time per op (GB/s).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="gqa_64k")
+    ap.add_argument("--splits", type=int, default=0, help="force the split count (0: planner policy)")
+    ap.add_argument("--flags", type=int, default=0, help="attn_decode_plan flags")
+    ap.add_argument("--replicas", type=int, default=0, help="KV pool copies to rotate (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step eagerly instead of from a captured graph (counter runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 20 device-to-device copies of MIB MiB (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, S):
+    """Bytes one stage-1 launch must move at minimum: every visible key of
+    every KV head once (V counted once when it aliases K), the page-table
+    entries, q, and the partial outputs + log-sum-exps it writes."""
+    es = w.elem_bytes
+    kv = w.logical_kv_bytes()
+    pt = sum(-(-c // w.page_size) for c in w.context_lens) * 4
+    q = w.batch * w.q_len * w.num_q_heads * w.head_dim_qk * es
+    rows = w.batch * w.q_len * w.num_q_heads
+    part = rows * S * (w.head_dim_v + 1) * 4
+    return kv, kv + pt + q + part
+
+
+def time_eager(fn_steps, steps, stream):
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            fn_steps(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), None
+
+
+def copy_probe(mib):
+    """A plain copy kernel of known size, for scaling HBM byte counters."""
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(20):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 20}), flush=True)
+
+
+def time_graph(fn_steps, steps, stream):
+    """Capture fn_steps(i) for i < steps into one graph; return (ms total)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            fn_steps(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):     # replay() launches on the current stream
+        g.replay()                      # untimed replay (graph upload, first touches)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), g
+
+
+def cpu_baseline(inp, kv_bytes, budget_s):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.decode_reference(inp)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 50:
+            break
+    med = float(np.median(times))
+    return {"value": kv_bytes / med / 1e9, "unit": "GB/s (logical KV bytes / oracle time per op)",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"whole decode op of the same workload, float64 NumPy oracle, {len(times)} runs, "
+                      f"median {med * 1e3:.1f} ms/op, host os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU split of the path is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    import split_kv_paged_page_amd as sk
+    from workloads import generate, get
+    from workloads.torch_io import upload
+
+    w = get(args.config)
+    inp = generate(w)
+    t = upload(inp, "cuda")
+    desc = sk.make_desc_from_tensors(t["q"], t["k_cache"], t["v_cache"], t["page_table"],
+                                     head_dim_v=w.head_dim_v, causal=w.causal)
+    plan = sk.attn_decode_plan(desc, int(max(w.context_lens)), args.splits or w.num_splits, args.flags)
+    S = plan.num_splits
+    kv_bytes, alg_bytes = algorithmic_bytes(w, S)
+    touched = w.unique_kv_bytes()
+    R = args.replicas or max(1, -(-(1 << 30) // touched))
+    ks = [t["k_cache"]] + [t["k_cache"].clone() for _ in range(R - 1)]
+    vs = [t["v_cache"]] + [t["v_cache"].clone() for _ in range(R - 1)] if t["v_cache"] is not None else ks
+    dt = torch.float32 if w.kv_dtype == "f32" else torch.bfloat16
+    out = torch.empty((w.batch, w.q_len, w.num_q_heads, w.head_dim_v), dtype=dt, device="cuda")
+    lse = torch.empty((w.batch, w.q_len, w.num_q_heads), dtype=torch.float32, device="cuda")
+    ws = torch.empty(plan.workspace_bytes // 4, dtype=torch.float32, device="cuda")
+    scale = float(inp.scale)
+    stream = torch.cuda.Stream()
+
+    def step(i):
+        r = i % R
+        sk.attn_decode_run(plan, t["q"], ks[r], vs[r], t["page_table"], t["context_lens"], scale, S,
+                           out, lse, ws, stream=stream.cuda_stream)
+
+    def stage1(i):
+        r = i % R
+        sk.attn_decode_partials(plan, t["q"], ks[r], vs[r], t["page_table"], t["context_lens"], scale, S,
+                                ws, stream=stream.cuda_stream)
+
+    # warmup (eager)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+
+    timer = time_eager if args.eager else time_graph
+    ms, g = timer(step, args.steps, stream)
+    del g
+    ms1, g1 = timer(stage1, args.steps, stream)
+    del g1
+    us_op = ms * 1e3 / args.steps
+    us_s1 = ms1 * 1e3 / args.steps
+    kv_gbs = kv_bytes / (us_op * 1e-6) / 1e9
+    ach = alg_bytes / (us_s1 * 1e-6) / 1e9
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"stage1_traffic_{w.name}.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("plan_key") == str(plan.key) and tr.get("kernel_source_hash") == source_hash():
+            traffic = tr.get("bytes_per_launch")
+
+    res = {
+        "metric": "split-KV decode: µs per decode op and KV GB/s as % of MI355X HBM peak",
+        "value": round(kv_gbs, 1),
+        "unit": "GB/s (logical KV bytes per decode op / whole-op time)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us_op / 1e3, 6),
+        "us_per_op": round(us_op, 3),
+        "kv_hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
+        "stage1_us": round(us_s1, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "f32",
+        "accumulate": "f32",
+        "data": "synthetic (seeded N(0,1) values, seeded page tables; no dataset)",
+        "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v,
+                   "page_size": w.page_size, "context": (w.context_lens[0] if len(set(w.context_lens)) == 1
+                                                        else list(w.context_lens)),
+                   "num_splits": S, "rows_per_wg": plan.rows_per_wg, "head_tiles": plan.head_tiles,
+                   "stage2_tiles": plan.stage2_tiles, "xcd_remap": plan.xcd_remap, "replicas": R,
+                   "kv_bytes_per_op": kv_bytes, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "stage1", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "alg_bytes_per_launch": alg_bytes, "launch_us": round(us_s1, 3)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, kv_bytes, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "split_kv_paged_page_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+/*
+ * attn_decode.h -- C ABI of libsplitkv: split-KV paged decode attention for
+ * MI355X (gfx950).
+ *
+ * The operation (aiter PR #4758, "[Gluon][MLA] Deeper async-copy pipeline in
+ * the bh16 stage-1 decode loop": Motivation and Technical Details items 1-3):
+ * every decode request's cached keys are cut into splits; a stage-1
+ * workgroup per (request, KV head, split) gathers its keys through the page
+ * table, scores them against all query rows that share the KV head (a GQA
+ * group, or all heads of an MLA latent head), keeps the running max and sum
+ * of the softmax and accumulates P.V, writing a normalised partial output and
+ * its log-sum-exp; stage 2 merges the splits of each query row by
+ * log-sum-exp.  For every (request b, query position j, query head h):
+ *
+ *     n      = ctx[b]                         (not causal)
+ *            = ctx[b] - q_len + 1 + j         (causal, bottom-right aligned)
+ *     s_t    = scale * <q[b,j,h,:], K_t[:Dk]>,     t in [0, n)
+ *     out    = sum_t e^(s_t - m) V_t / sum_t e^(s_t - m),   m = max_t s_t
+ *     lse    = m + ln sum_t e^(s_t - m)        (natural log; -inf if n = 0)
+ *
+ * with key t of request b stored at page page_table[b][t / P], slot t % P,
+ * and query head h reading KV head h / (H_q / H_kv).
+ *
+ * Split rule (host and device agree; attn_decode_split_range exposes it):
+ * chunk = A * ceil(ceil(ctx / S) / A) with A = split_align (64 keys); split s
+ * covers [s*chunk, min((s+1)*chunk, ctx)).  The 64-key block is the block
+ * the trip counts of the aiter PR's Test Result tables imply.
+ *
+ * Memory layouts (all device memory, caller-owned, element strides):
+ *   q            [B, q_len, H_q, Dk]  contiguous, dtype
+ *   k_cache      element (page, kvh, slot, d) at
+ *                page*k_stride_page + kvh*k_stride_head + slot*k_stride_tok + d
+ *   v_cache      same with v_strides; when v_aliases_k, V is K[..., :Dv] and
+ *                v_cache must equal k_cache
+ *   page_table   int32 [B, max_pages_per_req] row-major; entries past
+ *                ceil(ctx/P) are never read
+ *   context_lens int32 [B]
+ *   out          [B, q_len, H_q, Dv] contiguous, dtype
+ *   lse          float [B, q_len, H_q] (optional)
+ *   workspace    float o_part [B, q_len, H_q, S, Dv] at o_part_offset and
+ *                float lse_part [B, q_len, H_q, S] at lse_part_offset
+ *                (attn_decode_workspace_layout), S = the run's split count
+ *
+ * Threading and ownership: the library keeps no device memory and allocates
+ * nothing; run/partials/merge only validate host-side arguments, enqueue
+ * kernels on `stream` (a hipStream_t; NULL = the null stream) and return
+ * without synchronising, so they may be captured into a HIP graph.  Device
+ * data (page ids, context lengths) is not validated: page ids must lie in
+ * [0, num_pages) and 0 <= ctx <= max_pages_per_req * P (ctx >= q_len when
+ * causal), or the kernels read out of bounds.  The plan is a plain struct the
+ * caller owns and may copy.
+ *
+ * Errors: every call returns an attn_status; the thread-local text of the
+ * last failure is attn_decode_last_error().  No call aborts the process.
+ */
+#ifndef SPLITKV_ATTN_DECODE_H
+#define SPLITKV_ATTN_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_EINVAL = 1,        /* bad argument: null pointer, bad size or stride */
+  ATTN_EUNSUPPORTED = 2,  /* no kernel is built for this dtype/dims/layout */
+  ATTN_EWORKSPACE = 3,    /* num_splits above plan.max_splits, or workspace too small */
+  ATTN_EHIP = 4           /* HIP runtime error; text in attn_decode_last_error() */
+} attn_status;
+
+typedef enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Plan flags. */
+enum {
+  ATTN_PLAN_POLICY_P2 = 1,          /* split count = max(1, 256 / batch), the policy the
+                                       aiter PR's per-lever table was measured at */
+  ATTN_PLAN_NO_XCD_REMAP = 2,       /* keep the plain (split-minor) workgroup order */
+  ATTN_PLAN_NO_STAGE2_TILING = 4    /* one stage-2 workgroup per query row */
+};
+
+/* Kernel families the planner picks from. */
+enum {
+  ATTN_VARIANT_VALU = 1,            /* vector-ALU stage 1 (fewer than 16 rows per KV head) */
+  ATTN_VARIANT_MFMA = 2             /* matrix-core stage 1 (16 or more rows per KV head) */
+};
+
+/* Shape and layout of one decode call; filled by the caller. */
+typedef struct attn_decode_desc {
+  int32_t batch;              /* B >= 1 requests */
+  int32_t q_len;              /* query tokens per request (>= 1) */
+  int32_t num_q_heads;        /* H_q, a multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* H_kv */
+  int32_t head_dim_qk;        /* Dk */
+  int32_t head_dim_v;         /* Dv (<= Dk when v_aliases_k) */
+  int32_t page_size;          /* P keys per page */
+  int32_t max_pages_per_req;  /* page_table row length */
+  int32_t dtype;              /* attn_dtype of q, K, V and out */
+  int32_t causal;             /* 1: bottom-right causal among the q_len rows */
+  int32_t v_aliases_k;        /* 1: V = K[..., :Dv] (MLA latent cache) */
+  int32_t reserved;           /* must be 0 */
+  int64_t num_pages;          /* pages in the pool */
+  int64_t k_stride_page, k_stride_head, k_stride_tok;   /* elements */
+  int64_t v_stride_page, v_stride_head, v_stride_tok;   /* elements */
+} attn_decode_desc;
+
+/* What attn_decode_plan decided.  Plain data; no device memory. */
+typedef struct attn_decode_plan_t {
+  attn_decode_desc desc;
+  int32_t max_context_len;    /* largest ctx the plan was sized for */
+  int32_t num_splits;         /* S used when run is called with num_splits = 0 */
+  int32_t max_splits;         /* workspace is sized for up to this many splits */
+  int32_t split_align;        /* A, keys (64) */
+  int32_t variant;            /* ATTN_VARIANT_* */
+  int32_t rows_per_wg;        /* query rows one stage-1 workgroup scores */
+  int32_t head_tiles;         /* stage-1 workgroups per (request, KV head, split) */
+  int32_t stage2_tiles;       /* Dv slices per query row in stage 2 at num_splits */
+  int32_t xcd_remap;          /* 1: split-major, XCD-contiguous workgroup order */
+  int32_t flags;              /* ATTN_PLAN_* given to attn_decode_plan */
+  int64_t workspace_bytes;    /* bytes the caller must provide at max_splits */
+  uint64_t key;               /* hash of every field a kernel specialisation depends on */
+} attn_decode_plan_t;
+
+/*
+ * Plan a decode call.  Pure host function: checks the descriptor, picks the
+ * kernel variant, the split count S (num_splits > 0 forces it; 0 lets the
+ * policy choose so that about 256 CUs' worth of stage-1 workgroups exist,
+ * aiter PR #4758, Motivation), the workgroup order and the stage-2 tiling,
+ * and sizes the workspace for max(S, num_splits) splits.
+ * Returns ATTN_EINVAL / ATTN_EUNSUPPORTED on a bad or unsupported shape.
+ */
+attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_len,
+                             int32_t num_splits, int32_t flags, attn_decode_plan_t* plan);
+
+/*
+ * Full decode: stage 1 (partials into the workspace) then stage 2 (merge into
+ * out and, when lse is non-null, lse), both enqueued on `stream`.
+ * num_splits = 0 uses plan->num_splits; any value in [1, plan->max_splits]
+ * is allowed (results agree up to float rounding).  workspace_bytes must be
+ * at least the size attn_decode_workspace_layout reports for that split
+ * count.  scale multiplies q.k before the softmax.
+ */
+attn_status attn_decode_run(const attn_decode_plan_t* plan, const void* q,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* page_table, const int32_t* context_lens,
+                            float scale, int32_t num_splits, void* out, float* lse,
+                            void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Stage 1 only: writes o_part / lse_part of every split into the workspace
+ * (an empty split writes zeros and -inf).  Same arguments as run. */
+attn_status attn_decode_partials(const attn_decode_plan_t* plan, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* page_table, const int32_t* context_lens,
+                                 float scale, int32_t num_splits, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
+
+/* Stage 2 only: log-sum-exp merge of the num_splits partials held in the
+ * workspace (layout above) into out (plan dtype) and optional lse. */
+attn_status attn_decode_merge(const attn_decode_plan_t* plan, int32_t num_splits,
+                              const void* workspace, int64_t workspace_bytes,
+                              void* out, float* lse, void* stream);
+
+/* Byte offsets of o_part and lse_part inside the workspace and the total
+ * bytes needed for num_splits splits (0 = plan->num_splits). */
+attn_status attn_decode_workspace_layout(const attn_decode_plan_t* plan, int32_t num_splits,
+                                         int64_t* o_part_offset, int64_t* lse_part_offset,
+                                         int64_t* bytes);
+
+/* The split rule: [*begin, *end) of split `split` of `num_splits` (0 = the
+ * plan's) for a request with context_len keys.  Pure host function. */
+attn_status attn_decode_split_range(const attn_decode_plan_t* plan, int32_t context_len,
+                                    int32_t num_splits, int32_t split, int32_t* begin,
+                                    int32_t* end);
+
+/* Text of the calling thread's last error ("" if none).  Owned by the library;
+ * valid until the thread's next failing call. */
+const char* attn_decode_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITKV_ATTN_DECODE_H */

@@ -1,0 +1,103 @@
+// Device helpers for the gfx950 kernels: wave64 cross-lane reductions through
+// DPP, bf16 packing, the split rule and the XCD-aware workgroup order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace splitkv {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kNumXcd = 8;
+
+// DPP controls (GFX9 encoding).
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowNewBcast0 = 0x150;  // row_newbcast:n = 0x150 + n (gfx90a and later)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xf, 0xf, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+
+// Value of lane N of this lane's 16-lane row, for every lane of the row.
+template <int N>
+__device__ __forceinline__ float row_bcast_f32(float x) {
+  return dpp_f32<kDppRowNewBcast0 + N>(x);
+}
+template <int N>
+__device__ __forceinline__ int row_bcast_i32(int x) {
+  return dpp_i32<kDppRowNewBcast0 + N>(x);
+}
+
+// Max / sum over the 16 lanes of a DPP row; every lane of the row gets it.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f32<kDppQuadSwap1>(x));
+  x = fmaxf(x, dpp_f32<kDppQuadSwap2>(x));
+  x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f32<kDppQuadSwap1>(x);
+  x += dpp_f32<kDppQuadSwap2>(x);
+  x += dpp_f32<kDppRowHalfMirror>(x);
+  x += dpp_f32<kDppRowMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// fp32 -> bf16, nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  return (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                         c, false);
+}
+
+// 2^x; exact at 0, 0 for -inf.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Split rule: split s of S over ctx keys, chunk = A * ceil(ceil(ctx / S) / A).
+__device__ __forceinline__ void split_range(int ctx, int S, int A, int s, int& beg, int& end) {
+  int per = (ctx + S - 1) / S;
+  int chunk = ((per + A - 1) / A) * A;
+  if (chunk <= 0) chunk = A;
+  long long b = (long long)s * chunk;
+  long long e = b + chunk;
+  beg = (int)(b < ctx ? b : ctx);
+  end = (int)(e < ctx ? e : ctx);
+}
+
+// Workgroup order.  The dispatcher hands workgroup p to XCD p % 8; with the
+// remap on, XCD x receives one contiguous range of the logical (split-major)
+// order, so all requests' programs for one split land on one XCD's L2.  The
+// mapping is a bijection for any n (the first n % 8 XCDs take one extra).
+__device__ __forceinline__ int logical_wg(int p, int n, int remap) {
+  if (!remap) return p;
+  int q = n / kNumXcd, r = n % kNumXcd;
+  int x = p % kNumXcd, k = p / kNumXcd;
+  return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
+}  // namespace splitkv

@@ -1,0 +1,329 @@
+// Host side of libsplitkv: descriptor checks, the split policy, workspace
+// layout, and the stage-1 / stage-2 launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/attn_decode.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+attn_status fail(attn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+attn_status hip_fail(hipError_t e, const char* what) {
+  return fail(ATTN_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+constexpr int kSplitAlign = 64;   // keys per stage-1 block and split granule
+constexpr int kNumCu = 256;       // MI355X compute units
+constexpr int kMaxSplits = 4096;  // stage 2 keeps one weight per split in LDS
+
+uint64_t fnv1a(const void* p, size_t n, uint64_t h = 1469598103934665603ull) {
+  const unsigned char* c = static_cast<const unsigned char*>(p);
+  for (size_t i = 0; i < n; ++i) {
+    h ^= c[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+int elem_bytes(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+
+attn_status check_desc(const attn_decode_desc* d) {
+  if (!d) return fail(ATTN_EINVAL, "desc is null");
+  if (d->batch < 1 || d->q_len < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1)
+    return fail(ATTN_EINVAL, "batch, q_len and head counts must be >= 1");
+  if (d->num_q_heads % d->num_kv_heads)
+    return fail(ATTN_EINVAL, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)", d->num_q_heads,
+                d->num_kv_heads);
+  if (d->head_dim_qk < 1 || d->head_dim_v < 1 || d->page_size < 1 || d->max_pages_per_req < 1 ||
+      d->num_pages < 1)
+    return fail(ATTN_EINVAL, "head dims, page size, max_pages_per_req and num_pages must be >= 1");
+  if (d->dtype != ATTN_F32 && d->dtype != ATTN_BF16) return fail(ATTN_EINVAL, "unknown dtype %d", d->dtype);
+  if (d->causal != 0 && d->causal != 1) return fail(ATTN_EINVAL, "causal must be 0 or 1");
+  if (d->v_aliases_k != 0 && d->v_aliases_k != 1) return fail(ATTN_EINVAL, "v_aliases_k must be 0 or 1");
+  if (d->reserved != 0) return fail(ATTN_EINVAL, "reserved must be 0");
+  if (d->v_aliases_k && d->head_dim_v > d->head_dim_qk)
+    return fail(ATTN_EINVAL, "aliased V needs head_dim_v <= head_dim_qk");
+  const int64_t es = elem_bytes(d->dtype);
+  const int64_t ks[3] = {d->k_stride_page, d->k_stride_head, d->k_stride_tok};
+  const int64_t vs[3] = {d->v_stride_page, d->v_stride_head, d->v_stride_tok};
+  for (int i = 0; i < 3; ++i) {
+    if (ks[i] < 0 || vs[i] < 0) return fail(ATTN_EINVAL, "strides must be >= 0");
+    // Rows are read in 16-byte pieces (rocm-libraries PR #10102, Technical
+    // Details: 16-byte reads need a 16-byte-aligned pitch), so every row
+    // start must be 16-byte aligned.
+    if ((ks[i] * es) % 16 || (vs[i] * es) % 16)
+      return fail(ATTN_EUNSUPPORTED, "KV strides must be multiples of 16 bytes");
+  }
+  if (d->v_aliases_k && (vs[0] != ks[0] || vs[1] != ks[1] || vs[2] != ks[2]))
+    return fail(ATTN_EINVAL, "aliased V must use the K strides");
+  if (d->k_stride_tok < d->head_dim_qk || d->v_stride_tok < d->head_dim_v)
+    return fail(ATTN_EINVAL, "token stride is shorter than the head dim");
+  return ATTN_OK;
+}
+
+int pick_rows_per_wg(int dtype, int dk, int dv, int rows) {
+  for (int rt : {4, 8, 16})
+    if (rt >= rows && splitkv::stage1_valu_supported(dtype, dk, dv, rt)) return rt;
+  int best = 0;
+  for (int rt : {4, 8, 16})
+    if (splitkv::stage1_valu_supported(dtype, dk, dv, rt)) best = rt;
+  return best;
+}
+
+int pick_stage2_tiles(int rows2, int dv, bool allow) {
+  if (!allow) return 1;
+  // Slice the head dim only while the merge grid would leave CUs idle
+  // (aiter PR #4758, Technical Details item 3: up to 8 ways, fewer when the
+  // head dim does not divide evenly).
+  int t = 1;
+  while (t < 8 && rows2 * (t * 2) <= kNumCu && dv % (t * 2) == 0 && (dv / (t * 2)) % 4 == 0) t *= 2;
+  return t;
+}
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+void layout(const attn_decode_plan_t* p, int S, int64_t* o_off, int64_t* l_off, int64_t* bytes) {
+  const attn_decode_desc& d = p->desc;
+  const int64_t rows = (int64_t)d.batch * d.q_len * d.num_q_heads;
+  const int64_t ob = align256(rows * S * d.head_dim_v * 4);
+  if (o_off) *o_off = 0;
+  if (l_off) *l_off = ob;
+  if (bytes) *bytes = ob + align256(rows * S * 4);
+}
+
+attn_status resolve_splits(const attn_decode_plan_t* p, int32_t num_splits, int* S) {
+  if (!p) return fail(ATTN_EINVAL, "plan is null");
+  if (num_splits < 0) return fail(ATTN_EINVAL, "num_splits must be >= 0");
+  *S = num_splits ? num_splits : p->num_splits;
+  if (*S > p->max_splits)
+    return fail(ATTN_EWORKSPACE, "num_splits %d exceeds the plan's max_splits %d", *S, p->max_splits);
+  return ATTN_OK;
+}
+
+attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q, const void* k,
+                           const void* v, const int32_t* pt, const int32_t* ctx, float scale,
+                           void* ws, int64_t ws_bytes, hipStream_t st) {
+  const attn_decode_desc& d = plan->desc;
+  if (!q || !k || !v || !pt || !ctx || !ws) return fail(ATTN_EINVAL, "a device pointer is null");
+  if (d.v_aliases_k && v != k) return fail(ATTN_EINVAL, "aliased V: v_cache must equal k_cache");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) % 16 || (uintptr_t)ws % 256)
+    return fail(ATTN_EINVAL, "q/k/v must be 16-byte aligned and the workspace 256-byte aligned");
+  if (!(scale == scale)) return fail(ATTN_EINVAL, "scale is NaN");
+  int64_t o_off, l_off, need;
+  layout(plan, S, &o_off, &l_off, &need);
+  if (ws_bytes < need)
+    return fail(ATTN_EWORKSPACE, "workspace of %lld bytes is below the %lld needed", (long long)ws_bytes,
+                (long long)need);
+  splitkv::Stage1Params p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.page_table = pt;
+  p.ctx = ctx;
+  p.o_part = (float*)((char*)ws + o_off);
+  p.lse_part = (float*)((char*)ws + l_off);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.batch = d.batch;
+  p.q_len = d.q_len;
+  p.num_q_heads = d.num_q_heads;
+  p.num_kv_heads = d.num_kv_heads;
+  p.group = d.num_q_heads / d.num_kv_heads;
+  p.page_size = d.page_size;
+  p.max_pages = d.max_pages_per_req;
+  p.causal = d.causal;
+  p.num_splits = S;
+  p.split_align = plan->split_align;
+  p.rows_total = p.group * d.q_len;
+  p.rows_per_wg = plan->rows_per_wg;
+  p.head_tiles = plan->head_tiles;
+  p.xcd_remap = plan->xcd_remap;
+  const int64_t nwg = (int64_t)S * d.batch * d.num_kv_heads * plan->head_tiles;
+  if (nwg > 0x7fffffff) return fail(ATTN_EINVAL, "grid too large");
+  p.num_wgs = (int32_t)nwg;
+  p.ks_page = d.k_stride_page;
+  p.ks_head = d.k_stride_head;
+  p.ks_tok = d.k_stride_tok;
+  p.vs_page = d.v_stride_page;
+  p.vs_head = d.v_stride_head;
+  p.vs_tok = d.v_stride_tok;
+  hipError_t e = splitkv::launch_stage1_valu(p, d.dtype, d.head_dim_qk, d.head_dim_v, st);
+  if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
+  return ATTN_OK;
+}
+
+attn_status enqueue_stage2(const attn_decode_plan_t* plan, int S, const void* ws, int64_t ws_bytes,
+                           void* out, float* lse, hipStream_t st) {
+  const attn_decode_desc& d = plan->desc;
+  if (!ws || !out) return fail(ATTN_EINVAL, "workspace or out is null");
+  if ((uintptr_t)out % 16 || (uintptr_t)ws % 256 || (uintptr_t)lse % 4)
+    return fail(ATTN_EINVAL, "out must be 16-byte aligned and the workspace 256-byte aligned");
+  int64_t o_off, l_off, need;
+  layout(plan, S, &o_off, &l_off, &need);
+  if (ws_bytes < need)
+    return fail(ATTN_EWORKSPACE, "workspace of %lld bytes is below the %lld needed", (long long)ws_bytes,
+                (long long)need);
+  splitkv::Stage2Params p{};
+  p.o_part = (const float*)((const char*)ws + o_off);
+  p.lse_part = (const float*)((const char*)ws + l_off);
+  p.out = out;
+  p.lse = lse;
+  p.rows = d.batch * d.q_len * d.num_q_heads;
+  p.num_splits = S;
+  p.head_dim_v = d.head_dim_v;
+  p.tiles = pick_stage2_tiles(p.rows, d.head_dim_v, !(plan->flags & ATTN_PLAN_NO_STAGE2_TILING));
+  hipError_t e = splitkv::launch_stage2(p, d.dtype, st);
+  if (e != hipSuccess) return hip_fail(e, "stage-2 launch");
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_decode_last_error(void) { return g_err; }
+
+attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_len, int32_t num_splits,
+                             int32_t flags, attn_decode_plan_t* plan) {
+  if (!plan) return fail(ATTN_EINVAL, "plan is null");
+  attn_status st = check_desc(desc);
+  if (st != ATTN_OK) return st;
+  if (max_context_len < 0) return fail(ATTN_EINVAL, "max_context_len must be >= 0");
+  if ((int64_t)max_context_len > (int64_t)desc->max_pages_per_req * desc->page_size)
+    return fail(ATTN_EINVAL, "max_context_len %d exceeds max_pages_per_req * page_size", max_context_len);
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(ATTN_EINVAL, "num_splits must be in [0, %d]", kMaxSplits);
+  if (flags & ~(ATTN_PLAN_POLICY_P2 | ATTN_PLAN_NO_XCD_REMAP | ATTN_PLAN_NO_STAGE2_TILING))
+    return fail(ATTN_EINVAL, "unknown plan flags 0x%x", flags);
+
+  const attn_decode_desc& d = *desc;
+  const int rows = (d.num_q_heads / d.num_kv_heads) * d.q_len;
+  const int rt = pick_rows_per_wg(d.dtype, d.head_dim_qk, d.head_dim_v, rows);
+  if (!rt)
+    return fail(ATTN_EUNSUPPORTED, "no stage-1 kernel for dtype %d, head dims %d/%d", d.dtype, d.head_dim_qk,
+                d.head_dim_v);
+
+  attn_decode_plan_t p{};
+  p.desc = d;
+  p.max_context_len = max_context_len;
+  p.split_align = kSplitAlign;
+  p.variant = ATTN_VARIANT_VALU;
+  p.rows_per_wg = rt;
+  p.head_tiles = (rows + rt - 1) / rt;
+  p.flags = flags;
+  p.xcd_remap = (flags & ATTN_PLAN_NO_XCD_REMAP) ? 0 : 1;
+
+  // Split count.  The aiter PR's launcher gives each request about 256 /
+  // batch splits so that the 256 CUs stay busy (Motivation; Test Result
+  // table 1).  The default counts every stage-1 workgroup a split creates
+  // (KV heads and head tiles too) and never makes a split shorter than one
+  // 64-key block.
+  const int blocks = (max_context_len + kSplitAlign - 1) / kSplitAlign;
+  int S;
+  if (num_splits > 0) {
+    S = num_splits;
+  } else if (flags & ATTN_PLAN_POLICY_P2) {
+    S = kNumCu / d.batch;
+    if (S < 1) S = 1;
+  } else {
+    const int per_split = d.batch * d.num_kv_heads * p.head_tiles;
+    S = (2 * kNumCu) / per_split;
+    if (S > blocks) S = blocks;
+    if (S < 1) S = 1;
+  }
+  if (S > kMaxSplits) S = kMaxSplits;
+  p.num_splits = S;
+  p.max_splits = S;
+  p.stage2_tiles = pick_stage2_tiles(d.batch * d.q_len * d.num_q_heads, d.head_dim_v,
+                                     !(flags & ATTN_PLAN_NO_STAGE2_TILING));
+  if (!splitkv::stage2_supported(d.dtype, d.head_dim_v, p.stage2_tiles))
+    return fail(ATTN_EUNSUPPORTED, "no stage-2 kernel for head_dim_v %d", d.head_dim_v);
+  int64_t bytes;
+  layout(&p, p.max_splits, nullptr, nullptr, &bytes);
+  p.workspace_bytes = bytes;
+  // The key covers every field a kernel launch depends on (rocm-libraries
+  // PR #10102, Technical Details: a cache keyed on the kernel name alone
+  // missed the batch baked into the binary).
+  uint64_t h = fnv1a(&p.desc, sizeof(p.desc));
+  const int32_t fields[] = {p.max_context_len, p.num_splits, p.max_splits, p.split_align, p.variant,
+                            p.rows_per_wg,     p.head_tiles, p.stage2_tiles, p.xcd_remap, p.flags};
+  h = fnv1a(fields, sizeof(fields), h);
+  p.key = h;
+  *plan = p;
+  g_err[0] = 0;
+  return ATTN_OK;
+}
+
+attn_status attn_decode_workspace_layout(const attn_decode_plan_t* plan, int32_t num_splits,
+                                         int64_t* o_part_offset, int64_t* lse_part_offset, int64_t* bytes) {
+  int S;
+  attn_status st = resolve_splits(plan, num_splits, &S);
+  if (st != ATTN_OK) return st;
+  layout(plan, S, o_part_offset, lse_part_offset, bytes);
+  return ATTN_OK;
+}
+
+attn_status attn_decode_split_range(const attn_decode_plan_t* plan, int32_t context_len, int32_t num_splits,
+                                    int32_t split, int32_t* begin, int32_t* end) {
+  if (!begin || !end) return fail(ATTN_EINVAL, "begin/end is null");
+  if (!plan) return fail(ATTN_EINVAL, "plan is null");
+  if (num_splits < 0) return fail(ATTN_EINVAL, "num_splits must be >= 0");
+  const int S = num_splits ? num_splits : plan->num_splits;
+  if (context_len < 0) return fail(ATTN_EINVAL, "context_len must be >= 0");
+  if (split < 0 || split >= S) return fail(ATTN_EINVAL, "split %d outside [0, %d)", split, S);
+  const int64_t A = plan->split_align;
+  const int64_t per = (context_len + (int64_t)S - 1) / S;
+  int64_t chunk = (per + A - 1) / A * A;
+  if (chunk <= 0) chunk = A;
+  const int64_t b = (int64_t)split * chunk, e = b + chunk;
+  *begin = (int32_t)(b < context_len ? b : context_len);
+  *end = (int32_t)(e < context_len ? e : context_len);
+  return ATTN_OK;
+}
+
+attn_status attn_decode_partials(const attn_decode_plan_t* plan, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* page_table, const int32_t* context_lens,
+                                 float scale, int32_t num_splits, void* workspace, int64_t workspace_bytes,
+                                 void* stream) {
+  int S;
+  attn_status st = resolve_splits(plan, num_splits, &S);
+  if (st != ATTN_OK) return st;
+  return enqueue_stage1(plan, S, q, k_cache, v_cache, page_table, context_lens, scale, workspace,
+                        workspace_bytes, (hipStream_t)stream);
+}
+
+attn_status attn_decode_merge(const attn_decode_plan_t* plan, int32_t num_splits, const void* workspace,
+                              int64_t workspace_bytes, void* out, float* lse, void* stream) {
+  int S;
+  attn_status st = resolve_splits(plan, num_splits, &S);
+  if (st != ATTN_OK) return st;
+  return enqueue_stage2(plan, S, workspace, workspace_bytes, out, lse, (hipStream_t)stream);
+}
+
+attn_status attn_decode_run(const attn_decode_plan_t* plan, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* page_table, const int32_t* context_lens,
+                            float scale, int32_t num_splits, void* out, float* lse, void* workspace,
+                            int64_t workspace_bytes, void* stream) {
+  int S;
+  attn_status st = resolve_splits(plan, num_splits, &S);
+  if (st != ATTN_OK) return st;
+  if (!out) return fail(ATTN_EINVAL, "out is null");
+  st = enqueue_stage1(plan, S, q, k_cache, v_cache, page_table, context_lens, scale, workspace,
+                      workspace_bytes, (hipStream_t)stream);
+  if (st != ATTN_OK) return st;
+  return enqueue_stage2(plan, S, workspace, workspace_bytes, out, lse, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal launch parameters shared by the host library and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace splitkv {
+
+struct Stage1Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* page_table;
+  const int32_t* ctx;
+  float* o_part;          // [B, q_len, Hq, S, Dv]
+  float* lse_part;        // [B, q_len, Hq, S]
+  float scale_log2;       // scale * log2(e): scores are kept in base-2 units
+  int32_t batch, q_len, num_q_heads, num_kv_heads, group;
+  int32_t page_size, max_pages, causal;
+  int32_t num_splits, split_align;
+  int32_t rows_total;     // query rows per KV head = group * q_len
+  int32_t rows_per_wg, head_tiles;
+  int32_t xcd_remap;
+  int32_t num_wgs;        // S * B * Hkv * head_tiles
+  int64_t ks_page, ks_head, ks_tok;   // elements
+  int64_t vs_page, vs_head, vs_tok;
+};
+
+struct Stage2Params {
+  const float* o_part;
+  const float* lse_part;
+  void* out;
+  float* lse;             // may be null
+  int32_t rows;           // B * q_len * Hq
+  int32_t num_splits;
+  int32_t head_dim_v;
+  int32_t tiles;          // Dv slices per row
+};
+
+// Stage-1 launchers; return false when no kernel exists for the shape.
+bool stage1_valu_supported(int dtype, int dk, int dv, int rows_per_wg);
+hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, hipStream_t s);
+
+bool stage2_supported(int dtype, int dv, int tiles);
+hipError_t launch_stage2(const Stage2Params& p, int dtype, hipStream_t s);
+
+}  // namespace splitkv

@@ -1,0 +1,127 @@
+// Stage 2 of split-KV paged decode: log-sum-exp merge of the per-split
+// partials (aiter PR #4758, "[Gluon][MLA] Deeper async-copy pipeline in the
+// bh16 stage-1 decode loop", Technical Details item 3).
+//
+// One workgroup per (query row, Dv slice).  With few query rows (batch-1
+// decode) the host cuts the head dim into up to 8 slices so more CUs work;
+// each slice re-derives the row's max and weight sum on its own, so slices
+// never talk to each other and the result does not depend on the slicing.
+// Inside a workgroup, 256 threads = 16 split lanes x 16 four-float columns.
+#include "device_common.h"
+#include "launch.h"
+
+namespace splitkv {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr int kThreads = 256;
+constexpr int kMaxSplitsLds = 4096;
+constexpr int kSL = 16;                     // split lanes
+constexpr int kColSlots = kThreads / kSL;   // float4 columns per pass
+
+template <int DTYPE>
+__global__ __launch_bounds__(kThreads) void stage2_kernel(Stage2Params p) {
+  __shared__ float w_lds[kMaxSplitsLds];
+  __shared__ float red[kThreads / 64];
+  __shared__ __align__(16) float4 part[kThreads];
+
+  const int row = blockIdx.x / p.tiles;
+  const int tile = blockIdx.x % p.tiles;
+  const int S = p.num_splits;
+  const int dvt = p.head_dim_v / p.tiles;  // slice width, a multiple of 4
+  const int cols = dvt / 4;                // float4 columns in the slice
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+
+  const float* lse_row = p.lse_part + (int64_t)row * S;
+
+  // Row max over the splits.
+  float mx = kNegInf;
+  for (int s = tid; s < S; s += kThreads) mx = fmaxf(mx, lse_row[s]);
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float M = red[0];
+  for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, red[w]);
+  __syncthreads();
+
+  // Weights exp(lse_s - M) and their sum, in a fixed order.
+  float den = 0.f;
+  if (M != kNegInf) {
+    for (int s = tid; s < S; s += kThreads) {
+      const float wgt = fast_exp2((lse_row[s] - M) * kLog2e);
+      w_lds[s] = wgt;
+    }
+  }
+  __syncthreads();
+  if (M != kNegInf) {
+    for (int s = 0; s < S; ++s) den += w_lds[s];
+  }
+
+  // Thread (sl, cs): split lane sl sums splits sl, sl + kSL, ...; the kSL
+  // lane sums are then added in lane order.  kSL does not depend on the
+  // slicing, so sliced and unsliced merges give the same bits.
+  const int cs = tid % kColSlots, sl = tid / kColSlots;
+  const float* base = p.o_part + (int64_t)row * S * p.head_dim_v + tile * dvt;
+  for (int c0 = 0; c0 < cols; c0 += kColSlots) {
+    const int col = c0 + cs;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (M != kNegInf && col < cols) {
+      for (int s = sl; s < S; s += kSL) {
+        const float wgt = w_lds[s];
+        const float4 v = *(const float4*)(base + (int64_t)s * p.head_dim_v + col * 4);
+        a.x = fmaf(wgt, v.x, a.x);
+        a.y = fmaf(wgt, v.y, a.y);
+        a.z = fmaf(wgt, v.z, a.z);
+        a.w = fmaf(wgt, v.w, a.w);
+      }
+    }
+    part[tid] = a;
+    __syncthreads();
+    if (sl == 0 && col < cols) {
+      float4 t = part[cs];
+      for (int k = 1; k < kSL; ++k) {
+        const float4 u = part[k * kColSlots + cs];
+        t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+      }
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (M != kNegInf) {
+        const float inv = 1.f / den;
+        o = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+      }
+      const int64_t off = (int64_t)row * p.head_dim_v + tile * dvt + col * 4;
+      if constexpr (DTYPE == 0) {
+        *(float4*)((float*)p.out + off) = o;
+      } else {
+        uint2 pk;
+        pk.x = pack_bf16x2(o.x, o.y);
+        pk.y = pack_bf16x2(o.z, o.w);
+        *(uint2*)((uint16_t*)p.out + off) = pk;
+      }
+    }
+    __syncthreads();
+  }
+  if (p.lse && tile == 0 && tid == 0) p.lse[row] = M == kNegInf ? kNegInf : M + __logf(den);
+}
+
+}  // namespace
+
+bool stage2_supported(int dtype, int dv, int tiles) {
+  if (dtype != 0 && dtype != 1) return false;
+  if (tiles < 1 || dv % tiles) return false;
+  const int dvt = dv / tiles;
+  return dvt % 4 == 0;
+}
+
+hipError_t launch_stage2(const Stage2Params& p, int dtype, hipStream_t st) {
+  if (p.num_splits > kMaxSplitsLds) return hipErrorInvalidValue;
+  const dim3 grid(p.rows * p.tiles);
+  if (dtype == 0)
+    hipLaunchKernelGGL(stage2_kernel<0>, grid, dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL(stage2_kernel<1>, grid, dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace splitkv

@@ -1,0 +1,180 @@
+"""The C ABI on the host (no GPU): the library loads and exports every
+function include/attn_decode.h declares, the ctypes structs match the C
+layout, the planner's split rule equals the oracle's, the P2 policy mode
+reproduces the split counts of aiter PR #4758's Test Result table 1, plan
+keys cover every shape field, and invalid arguments come back as status
+codes with a message (no kernel is launched on any of these paths)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import split_kv_paged_page_amd as sk
+from tests.test_oracle import read_table
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_decode.h")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:attn_status|const char\*)\s+(attn_\w+)\s*\(", txt, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 7
+    L = sk.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(sk.EXPORTED) == names
+    out = subprocess.run(["nm", "-D", "--defined-only", sk.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, re.M), n
+
+
+def test_struct_layout_matches_header(tmp_path):
+    fields_d = [f for f, _ in sk.AttnDecodeDesc._fields_]
+    fields_p = [f for f, _ in sk.AttnDecodePlan._fields_]
+    src = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void){",
+           'printf("%zu %zu\\n", sizeof(attn_decode_desc), sizeof(attn_decode_plan_t));']
+    for f in fields_d:
+        src.append(f'printf("d {f} %zu\\n", offsetof(attn_decode_desc, {f}));')
+    for f in fields_p:
+        src.append(f'printf("p {f} %zu\\n", offsetof(attn_decode_plan_t, {f}));')
+    src.append("return 0;}")
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", str(c), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    sd, sp = map(int, lines[0].split())
+    assert sd == ctypes.sizeof(sk.AttnDecodeDesc) and sp == ctypes.sizeof(sk.AttnDecodePlan)
+    for ln in lines[1:]:
+        if not ln:
+            continue
+        kind, f, off = ln.split()
+        cls = sk.AttnDecodeDesc if kind == "d" else sk.AttnDecodePlan
+        assert getattr(cls, f).offset == int(off), (kind, f)
+
+
+def desc(B=1, q_len=1, Hq=16, Hkv=2, Dk=128, Dv=128, P=16, maxp=4096, dtype=sk.ATTN_BF16, causal=0,
+         alias=0, pages=8192):
+    ks = (Hkv * P * Dk, P * Dk, Dk)
+    vs = ks if alias else (Hkv * P * Dv, P * Dv, Dv)
+    return sk.make_desc(batch=B, q_len=q_len, num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=Dk,
+                        head_dim_v=Dv, page_size=P, max_pages_per_req=maxp, dtype=dtype, causal=causal,
+                        v_aliases_k=alias, num_pages=pages, k_strides=ks, v_strides=vs)
+
+
+def mla_desc(B):
+    return desc(B=B, Hq=16, Hkv=1, Dk=576, Dv=512, P=1, maxp=68000, alias=1, pages=655360)
+
+
+def test_plan_split_rule_equals_oracle():
+    rng = np.random.default_rng(0)
+    p = sk.attn_decode_plan(desc(), 65536, 0)
+    for L in list(range(0, 300)) + list(rng.integers(0, 65536, 300)):
+        for S in (1, 2, 3, 5, 7, 64, 128, 333):
+            ref = oracle.split_bounds(int(L), S, 64)
+            for s in range(S):
+                assert sk.attn_decode_split_range(p, int(L), S, s) == ref[s]
+
+
+def test_p2_policy_reproduces_table():
+    ctx, rows = read_table("aiter4758_policy_table.txt")
+    for r in rows:
+        p = sk.attn_decode_plan(mla_desc(r["conc"]), ctx, 0, sk.ATTN_PLAN_POLICY_P2)
+        assert p.num_splits == r["splits"], r
+        b, e = sk.attn_decode_split_range(p, ctx, 0, 0)
+        assert (e - b) // 64 == r["trips"] and (e - b) % 64 == 0
+
+
+def test_default_policy_fills_the_chip():
+    p = sk.attn_decode_plan(desc(), 65536, 0)
+    wgs = p.num_splits * 1 * 2 * p.head_tiles
+    assert wgs >= 256
+    p = sk.attn_decode_plan(desc(), 100, 0)      # short context: never more splits than 64-key blocks
+    assert p.num_splits == 2
+
+
+def test_plan_key_covers_shape_fields():
+    # rocm-libraries PR #10102, Technical Details: two configurations that differ only in
+    # batch shared a launcher-cache entry; every descriptor field must reach the key.
+    base = sk.attn_decode_plan(desc(B=4, maxp=2048), 2048, 8).key
+    keys = {base}
+    for kw in (dict(B=6), dict(maxp=2049), dict(Hq=32), dict(P=32, maxp=1024), dict(causal=1),
+               dict(pages=9000), dict(dtype=sk.ATTN_F32)):
+        args = dict(B=4, maxp=2048)
+        args.update(kw)
+        if args.get("dtype") == sk.ATTN_F32:
+            args.update(Dk=128, Dv=128)
+        k = sk.attn_decode_plan(desc(**args), 2048, 8).key
+        assert k not in keys, kw
+        keys.add(k)
+    assert sk.attn_decode_plan(desc(B=4, maxp=2048), 2048, 16).key != base
+    assert sk.attn_decode_plan(desc(B=4, maxp=2048), 2048, 8, sk.ATTN_PLAN_NO_XCD_REMAP).key != base
+    assert sk.attn_decode_plan(desc(B=4, maxp=2048), 2048, 8).key == base
+
+
+def test_workspace_layout():
+    p = sk.attn_decode_plan(desc(), 65536, 128)
+    o, l_, b = sk.attn_decode_workspace_layout(p, 0)
+    rows = 16
+    assert o == 0 and l_ == rows * 128 * 128 * 4 and b >= l_ + rows * 128 * 4 and b == p.workspace_bytes
+    _, _, b64 = sk.attn_decode_workspace_layout(p, 64)
+    assert b64 < b
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (dict(Hq=15), sk.ATTN_EINVAL),
+    (dict(B=0), sk.ATTN_EINVAL),
+    (dict(Dk=96, Dv=96), sk.ATTN_EUNSUPPORTED),
+    (dict(dtype=7), sk.ATTN_EINVAL),
+    (dict(alias=1, Dv=256), sk.ATTN_EINVAL),
+])
+def test_plan_rejects(mutate, status):
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_plan(desc(**mutate), 1024, 0)
+    assert ei.value.status == status
+    assert sk.attn_decode_last_error()
+
+
+def test_plan_rejects_misaligned_stride():
+    d = desc()
+    d.k_stride_tok = 129          # 258-byte rows break 16-byte alignment
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_plan(d, 1024, 0)
+    assert ei.value.status == sk.ATTN_EUNSUPPORTED
+
+
+def test_plan_rejects_context_beyond_page_table():
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_plan(desc(maxp=10), 161, 0)
+    assert ei.value.status == sk.ATTN_EINVAL
+
+
+def test_run_argument_errors_before_any_launch():
+    p = sk.attn_decode_plan(desc(), 65536, 8)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_run(p, fake, fake, fake, fake, fake, 0.1, 9, fake, None, fake, 1 << 30, stream=0)
+    assert ei.value.status == sk.ATTN_EWORKSPACE
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_run(p, None, fake, fake, fake, fake, 0.1, 0, fake, None, fake, 1 << 30, stream=0)
+    assert ei.value.status == sk.ATTN_EINVAL
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_run(p, fake, fake, fake, fake, fake, 0.1, 0, fake, None, fake, 16, stream=0)
+    assert ei.value.status == sk.ATTN_EWORKSPACE
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_run(p, fake + 8, fake, fake, fake, fake, 0.1, 0, fake, None, fake, 1 << 30, stream=0)
+    assert ei.value.status == sk.ATTN_EINVAL
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_run(p, fake, fake, fake, fake, fake, float("nan"), 0, fake, None, fake, 1 << 30, stream=0)
+    assert ei.value.status == sk.ATTN_EINVAL

@@ -1,0 +1,267 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances: max over output rows of max|y - y_ref| / max|y_ref| <= 1e-2 for
+bf16 inputs (fp32 accumulation, bf16 output) and <= 1e-5 for fp32; final and
+per-split log-sum-exp within 1e-3 absolute, -inf exactly where a row or split
+has no visible key.  Page gather and split boundaries are checked bit-exactly
+with the one-hot construction.  Outputs and workspace are NaN-filled before
+every run, so a value the kernels skip cannot pass.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_helpers import Decode, lse_err, row_rel_err, say, tol_for
+from workloads import generate, get, scaled
+from workloads.gen import designate
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def small_cases():
+    return {
+        "gqa_tiny_f32": get("gqa_tiny_f32"),
+        "gqa_64k_s5000": scaled("gqa_64k", context_lens=(5000,), pool_pages=1024),
+        "gqa_64k_b3_ragged": scaled("gqa_64k", context_lens=(1, 777, 4100), pool_pages=1024, seed=21),
+        "mla_b48_b16": scaled("mla_b48", batch=16, context_lens=(1000,) * 16, prefix_len=700),
+        "mla_wide_b4": scaled("mla_wide", context_lens=(777, 1, 300, 2049)),
+        "varlen_drafts": get("varlen_drafts"),
+    }
+
+
+_INPUTS = {}
+
+
+def inputs(name, w):
+    if name not in _INPUTS:
+        _INPUTS[name] = generate(w)
+    return _INPUTS[name]
+
+
+def check_against_oracle(d: Decode, tol, S=None, requests=None, check_splits=True):
+    inp = d.inp
+    S = S or d.S
+    ro, rl = oracle.decode_reference(inp, requests=requests)
+    sel = slice(None) if requests is None else list(requests)
+    e_out = row_rel_err(d.out_f64()[sel], ro[sel])
+    e_lse = lse_err(d.lse_f64()[sel], rl[sel])
+    assert e_out <= tol, f"output rel err {e_out:.3e} > {tol}"
+    assert e_lse <= 1e-3, f"lse err {e_lse:.3e}"
+    if check_splits:
+        po, pl = oracle.split_reference(inp, S, requests=requests)
+        go, gl = d.split_parts(S)
+        gl_ = gl[sel]
+        go_ = go[sel]
+        e_po = row_rel_err(go_, po[sel])
+        e_pl = lse_err(gl_, pl[sel])
+        assert e_po <= tol, f"per-split output rel err {e_po:.3e}"
+        assert e_pl <= 1e-3, f"per-split lse err {e_pl:.3e}"
+        # planted mistake in the oracle: a split rule on 32-key blocks must not
+        # agree with the kernel wherever the two rules differ
+        if S > 1:
+            bo, bl = oracle.split_reference(inp, S, A=32, requests=requests)
+            differs = any(oracle.split_bounds(int(L), S, 32) != oracle.split_bounds(int(L), S, 64)
+                          for L in (inp.context_lens if requests is None else inp.context_lens[list(requests)]))
+            if differs:
+                fin = np.isfinite(bl[sel]) & np.isfinite(gl_)
+                assert np.max(np.abs(bl[sel][fin] - gl_[fin]), initial=0) > 1e-3 or \
+                    np.isneginf(bl[sel]).sum() != np.isneginf(gl_).sum()
+    return e_out, e_lse
+
+
+@pytest.mark.parametrize("name", list(small_cases()))
+def test_parity_small(name):
+    w = small_cases()[name]
+    inp = inputs(name, w)
+    say(f"parity_small {name} B={w.batch} ctx={w.context_lens[:4]} seed={w.seed} run")
+    d = Decode(inp, num_splits=w.num_splits).run()
+    e_out, e_lse = check_against_oracle(d, tol_for(w))
+    print(f"{name}: S={d.S} rows/wg={d.plan.rows_per_wg} tiles={d.plan.head_tiles} "
+          f"out {e_out:.2e} lse {e_lse:.2e}")
+
+
+@pytest.mark.parametrize("name,splits", [("gqa_tiny_f32", (1, 2, 4, 7, 16)),
+                                         ("gqa_64k_s5000", (1, 3, 64, 79, 200)),
+                                         ("varlen_drafts", (1, 5, 33)),
+                                         ("mla_b48_b16", (2, 17))])
+def test_parity_forced_splits(name, splits):
+    w = small_cases()[name]
+    inp = inputs(name, w)
+    d = Decode(inp, max_splits=max(splits))
+    for S in splits:
+        say(f"forced_splits {name} S={S}")
+        d.S = S
+        d.run(S)
+        check_against_oracle(d, tol_for(w), S=S)
+
+
+def test_empty_contexts_and_splits():
+    w = scaled("gqa_64k", context_lens=(0, 5, 64, 65, 0, 130), pool_pages=64, seed=9)
+    inp = generate(w)
+    say("empty contexts S=4")
+    d = Decode(inp, num_splits=4).run()
+    check_against_oracle(d, tol_for(w))
+    out, lse = d.out_f64(), d.lse_f64()
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    assert np.all(out[4] == 0) and np.all(np.isneginf(lse[4]))
+
+
+def designated_tokens(inp, S, where):
+    """Per request and KV head, one designated key per split: the first or
+    the last key every query row of the request can see in that split."""
+    w = inp.w
+    toks = []
+    for b in range(w.batch):
+        L = int(inp.context_lens[b])
+        n0 = oracle.visible_keys(L, w.q_len, 0, w.causal)
+        per_head = []
+        for h in range(w.num_kv_heads):
+            ts = []
+            for (sb, se) in oracle.split_bounds(L, S):
+                e = min(se, n0)
+                if e <= sb:
+                    continue
+                if where == "first":
+                    ts.append(min(sb + h, e - 1))
+                else:
+                    ts.append(max(e - 1 - h, sb))
+            per_head.append(ts)
+        toks.append(per_head)
+    return toks
+
+
+@pytest.mark.parametrize("name", ["gqa_tiny_f32", "gqa_64k_b3_ragged", "mla_b48_b16", "mla_wide_b4",
+                                  "varlen_drafts"])
+@pytest.mark.parametrize("where", ["first", "last"])
+def test_bitexact_gather_and_boundaries(name, where):
+    """One-hot: the designated key of each split scores 2*dims above all
+    others, so its weight is exactly 1 and every other weight is 0; each
+    split's o_part must then be that key's V row bit for bit."""
+    w = small_cases()[name]
+    base = inputs(name, w)
+    probe = Decode(base, num_splits=w.num_splits)
+    S = probe.S
+    del probe
+    toks = designated_tokens(base, S, where)
+    inp = designate(base, toks)
+    say(f"bitexact {name} {where} S={S}")
+    d = Decode(inp, num_splits=S).run()
+    go, gl = d.split_parts()
+    g = w.num_q_heads // w.num_kv_heads
+    score_dims = w.head_dim_qk - (w.head_dim_v if w.v_aliases_k else 0)
+    P = w.page_size
+    checked = 0
+    for b in range(w.batch):
+        L = int(inp.context_lens[b])
+        bounds = oracle.split_bounds(L, S)
+        for kvh in range(w.num_kv_heads):
+            for t in toks[b][kvh]:
+                s = next(i for i, (sb, se) in enumerate(bounds) if sb <= t < se)
+                page, slot = inp.page_table[b, t // P], t % P
+                src = inp.k_cache if w.v_aliases_k else inp.v_cache
+                vrow = oracle.to_f64(src[page, kvh, slot, :w.head_dim_v], w.kv_dtype)
+                for j in range(w.q_len):
+                    for hh in range(g):
+                        h = kvh * g + hh
+                        np.testing.assert_array_equal(go[b, j, h, s], vrow,
+                                                      err_msg=f"b={b} kvh={kvh} t={t} split={s} j={j} h={h}")
+                        assert abs(gl[b, j, h, s] - score_dims) <= 1e-6 * score_dims
+                        checked += 1
+    assert checked > 0
+
+
+def test_bit_identity_of_relabellings():
+    """XCD-aware order, stage-2 slicing and physical page placement change
+    no bits (aiter PR #4758, Technical Details items 2 and 3)."""
+    import split_kv_paged_page_amd as sk
+    for name in ("gqa_64k_b3_ragged", "mla_b48_b16"):
+        w = small_cases()[name]
+        inp = inputs(name, w)
+        say(f"relabel {name} default")
+        a = Decode(inp).run()
+        ref_out, ref_lse, ref_ws = a.out.cpu(), a.lse.cpu(), a.used_ws_bits()
+        for flags in (sk.ATTN_PLAN_NO_XCD_REMAP, sk.ATTN_PLAN_NO_STAGE2_TILING,
+                      sk.ATTN_PLAN_NO_XCD_REMAP | sk.ATTN_PLAN_NO_STAGE2_TILING):
+            say(f"relabel {name} flags={flags}")
+            bdec = Decode(inp, num_splits=a.S, flags=flags).run()
+            assert torch.equal(bdec.out.cpu(), ref_out)
+            assert torch.equal(bdec.lse.cpu(), ref_lse)
+            assert np.array_equal(bdec.used_ws_bits(), ref_ws)
+        # physical page permutation with the page table remapped
+        rng = np.random.default_rng(5)
+        perm = rng.permutation(inp.k_cache.shape[0])
+        k2 = np.empty_like(inp.k_cache)
+        k2[perm] = inp.k_cache
+        v2 = None
+        if inp.v_cache is not None:
+            v2 = np.empty_like(inp.v_cache)
+            v2[perm] = inp.v_cache
+        pt2 = perm[inp.page_table].astype(np.int32)
+        say(f"relabel {name} page permutation")
+        c = Decode(inp.with_(k_cache=k2, v_cache=v2, page_table=pt2), num_splits=a.S).run()
+        assert torch.equal(c.out.cpu(), ref_out)
+        assert torch.equal(c.lse.cpu(), ref_lse)
+
+
+def test_run_equals_partials_then_merge_and_is_deterministic():
+    w = small_cases()["gqa_64k_s5000"]
+    inp = inputs("gqa_64k_s5000", w)
+    say("run vs partials+merge")
+    d = Decode(inp).run()
+    out, lse, ws = d.out.clone(), d.lse.clone(), d.used_ws_bits()
+    d.poison()
+    d.partials()
+    d.merge()
+    assert torch.equal(d.out, out) and torch.equal(d.lse, lse) and np.array_equal(d.used_ws_bits(), ws)
+    for _ in range(5):
+        d.run()
+        assert torch.equal(d.out, out) and np.array_equal(d.used_ws_bits(), ws)
+
+
+@pytest.mark.parametrize("name", ["gqa_tiny_f32", "gqa_64k_s5000", "varlen_drafts"])
+def test_stage2_alone_on_oracle_partials(name):
+    """Merge oracle partials (rounded to fp32) on the GPU; compare with the
+    oracle's float64 merge of the same rounded partials."""
+    w = small_cases()[name]
+    inp = inputs(name, w)
+    d = Decode(inp, num_splits=w.num_splits or 9)
+    S = d.S
+    po, pl = oracle.split_reference(inp, S)
+    po32, pl32 = po.astype(np.float32), pl.astype(np.float32)
+    import split_kv_paged_page_amd as sk
+    o_off, l_off, _ = sk.attn_decode_workspace_layout(d.plan, S)
+    d.poison()
+    ws = d.ws
+    ws[o_off // 4: o_off // 4 + po32.size] = torch.from_numpy(po32.ravel()).cuda()
+    ws[l_off // 4: l_off // 4 + pl32.size] = torch.from_numpy(pl32.ravel()).cuda()
+    say(f"stage2 alone {name} S={S}")
+    d.merge()
+    mo, ml = oracle.merge_reference(po32.astype(np.float64), pl32.astype(np.float64))
+    tol = 1e-5 if w.kv_dtype == "f32" else 1e-2
+    assert row_rel_err(d.out_f64(), mo) <= tol
+    assert lse_err(d.lse_f64(), ml) <= 1e-5
+
+
+# ---- full sizes, policy split count (the launch configuration the benchmark times) ----
+
+FULL = [("gqa_64k", None), ("varlen_drafts", None), ("mla_b48", (0, 13, 47)),
+        ("mla_wide", (0, 63)), ("mla_b48_ctl", (5, 40))]
+
+
+@pytest.mark.parametrize("name,requests", FULL)
+def test_parity_full_size_sampled(name, requests):
+    w = get(name)
+    say(f"full-size {name}: generating inputs")
+    inp = generate(w)
+    say(f"full-size {name}: run")
+    d = Decode(inp).run()
+    e_out, e_lse = check_against_oracle(d, tol_for(w), requests=requests, check_splits=requests is None)
+    print(f"{name}: S={d.S} out {e_out:.2e} lse {e_lse:.2e}")
+    if requests is not None:
+        # every other request: outputs written, finite, lse finite
+        assert not torch.isnan(d.out).any() and torch.isfinite(d.lse).all()
