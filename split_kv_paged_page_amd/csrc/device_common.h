@@ -10,6 +10,10 @@ namespace splitkv {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+// Read-only words in the constant address space (uniform loads from it
+// compile to s_load).
+typedef const __attribute__((address_space(4))) uint32_t qconst_t;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kNumXcd = 8;
@@ -77,6 +81,21 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 // 2^x; exact at 0, 0 for -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
+// at lds + 16 * i (the LDS base is wave-uniform; it goes through M0).
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (GFX9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
 
 // Split rule: split s of S over ctx keys, chunk = A * ceil(ceil(ctx / S) / A).
 __device__ __forceinline__ void split_range(int ctx, int S, int A, int s, int& beg, int& end) {

@@ -6,7 +6,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/attn_decode.h"
+#include "attn_decode.h"
 #include "launch.h"
 
 namespace {
@@ -71,6 +71,12 @@ attn_status check_desc(const attn_decode_desc* d) {
     return fail(ATTN_EINVAL, "aliased V must use the K strides");
   if (d->k_stride_tok < d->head_dim_qk || d->v_stride_tok < d->head_dim_v)
     return fail(ATTN_EINVAL, "token stride is shorter than the head dim");
+  // Kernels address a row as a 32-bit count of 16-byte units from the head's
+  // base (pools up to 64 GiB).
+  const int64_t kmax = ((d->num_pages - 1) * ks[0] + (int64_t)(d->page_size - 1) * ks[2]) * es / 16;
+  const int64_t vmax = ((d->num_pages - 1) * vs[0] + (int64_t)(d->page_size - 1) * vs[2]) * es / 16;
+  if (kmax >= (int64_t(1) << 32) || vmax >= (int64_t(1) << 32))
+    return fail(ATTN_EUNSUPPORTED, "KV pool spans more than 64 GiB");
   return ATTN_OK;
 }
 

@@ -3,22 +3,35 @@
 // One workgroup scores one split of one request's keys against RT query rows
 // that share a KV head (aiter PR #4758, "[Gluon][MLA] Deeper async-copy
 // pipeline in the bh16 stage-1 decode loop", Motivation: each stage-1
-// program walks its split's KV blocks).  Rows per KV head below 16 are too
-// few for a dense matrix-core contraction, so this kernel stays on the VALU.
+// program walks its split's KV blocks).  Fewer than 16 rows per KV head are
+// too few for a dense matrix-core contraction, so this kernel stays on VALU.
 //
-// Work split inside a workgroup: NW waves take 64-key blocks of the split in
-// turn, each with its own running max / sum / accumulator, merged at the end.
-// Inside a wave:
-//   * Q.K: lane t owns key t of the block and forms all RT dot products
-//     against the query rows held in LDS (every lane reads the same q chunk,
-//     an LDS broadcast);
-//   * softmax: each 16-lane DPP row keeps its own running max per query row
-//     (max over the row by DPP, TensorFold PR #1932's fold-by-DPP approach on
-//     wave64's 16-lane rows), so no cross-row traffic happens in the loop;
-//   * P.V: the 16 lanes of row g accumulate keys 16g..16g+15 of the block;
-//     lane x owns a contiguous slice of the head dim, so every V row is read
-//     as one coalesced 256-byte (or wider) segment, and the weight of key i
-//     reaches the row's lanes through row_newbcast:i.
+// NW waves take 64-key blocks of the split in turn, each with its own
+// running max / sum / accumulator, merged at the end.  Per wave and block:
+//   * page walk: lane t looks up key t's page once and turns it into 32-bit
+//     row offsets (16-byte units) for K and V; keys past the visible end are
+//     clamped to the last visible key and later get weight 0, so every load
+//     is unconditional and all of a block's loads are in flight together;
+//   * K: one direct-to-LDS 16-byte load per lane (global_load_lds_dwordx4)
+//     moves 4 (or 2) whole rows per instruction, coalesced, into a 1 KB LDS
+//     group; groups are padded by 16 bytes, which spreads the lane-per-key
+//     reads below over all 64 banks at 4 lanes per bank, the ds_read_b128
+//     floor.  A per-row pad is impossible because one instruction fills
+//     several rows contiguously; the pad goes between load groups, as
+//     rocm-libraries PR #10102 does for its head-dim-64 K tile (Motivation
+//     bank table, Technical Details);
+//   * Q.K: lane t owns key t and forms all RT dot products; the query rows are
+//     wave-uniform and sit in SGPRs (scalar loads), the scalar operand of
+//     v_dot2 / v_fma, so they cost no LDS bandwidth;
+//   * softmax: each 16-lane DPP row keeps its own running max per query row;
+//   * P.V: the 16 lanes of DPP row g accumulate keys 16g..16g+15; lane x owns
+//     a contiguous slice of the head dim, so V rows arrive as coalesced
+//     256-byte (or wider) segments, and key i's weight reaches the row's
+//     lanes through row_newbcast:i.  For bf16 the weights of a key pair are
+//     rounded to one bf16x2 and both keys go through one v_dot2_f32_bf16 per
+//     output element (fp32 accumulation); fp32 inputs keep fp32 weights.
+#include <utility>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -29,25 +42,37 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 
 template <int DTYPE, int DK, int DV, int RT, int NW>
-__global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
-  constexpr int ES = DTYPE == 0 ? 4 : 2;  // element bytes
-  constexpr int KRB = DK * ES;            // bytes of one K row
-  constexpr int VRB = DV * ES;            // bytes of one V row
-  constexpr int KCH = KRB / 16;           // 16-byte chunks of a K row
-  constexpr int VU4 = VRB / 256;          // 16-byte loads per lane per V row
-  constexpr int VE = VU4 * 16 / ES;       // V elements a lane owns
+struct Cfg {
+  static constexpr int ES = DTYPE == 0 ? 4 : 2;  // element bytes
+  static constexpr int KRB = DK * ES;            // bytes of one K row
+  static constexpr int VRB = DV * ES;            // bytes of one V row
+  static constexpr int KCH = KRB / 16;           // 16-byte chunks of a K row
+  static constexpr bool KLDS = KCH <= 64 && 64 % KCH == 0;  // K through the LDS tile
+  static constexpr int RPI = KLDS ? 64 / KCH : 0;           // K rows per load instruction
+  static constexpr int KINS = KLDS ? KCH : 0;               // load instructions per 64 rows
+  static constexpr int GP = 64 * 16 + 16;        // LDS pitch of one load group (1 KB + pad)
+  static constexpr int VU4 = VRB / 256;          // 16-byte loads per lane per V row
+  static constexpr int VE = VU4 * 16 / ES;       // V elements a lane owns
+  static constexpr int KTILE = KLDS ? KINS * GP : 0;
+  static constexpr int PART = 4 * RT * DV * 4 + 4 * RT * 2 * 4;  // 4 DPP rows: acc, then m, l
+  static constexpr int WAVE_B = ((KTILE > PART ? KTILE : PART) + 15) / 16 * 16;
+  static constexpr int SMEM = NW * WAVE_B;
   static_assert(VRB % 256 == 0 && KRB % 16 == 0, "row sizes");
   static_assert(RT * VE <= 128, "accumulator budget");
+};
 
-  __shared__ __align__(16) uint8_t q_lds[RT * KRB];
-  __shared__ float comb_m[NW][RT];
-  __shared__ float comb_l[NW][RT];
-  __shared__ __align__(16) float comb_acc[NW][RT][DV];
+template <int DTYPE, int DK, int DV, int RT, int NW>
+__global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
+  using C = Cfg<DTYPE, DK, DV, RT, NW>;
+  constexpr int ES = C::ES, KRB = C::KRB, KCH = C::KCH, VU4 = C::VU4, VE = C::VE;
+
+  __shared__ __align__(16) uint8_t smem[C::SMEM];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;
   const int x = lane & 15;
+  uint8_t* wave_lds = smem + wave * C::WAVE_B;
 
   int lid = logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap);
   const int tile = lid % p.head_tiles;
@@ -77,20 +102,32 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
     end_max = e > end_max ? e : end_max;
   }
 
-  // Query rows of this tile into LDS (zeros for rows past the group).
-  for (int c = threadIdx.x; c < RT * KCH; c += 64 * NW) {
-    const int r = c / KCH, cc = c % KCH;
-    const int gr = tile * RT + r;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (gr < p.rows_total) {
-      const int j = gr / p.group, h = kvh * p.group + gr % p.group;
-      const uint8_t* src = (const uint8_t*)p.q +
-                           ((((int64_t)b * p.q_len + j) * p.num_q_heads + h) * DK) * ES + cc * 16;
-      val = *(const uint4*)src;
-    }
-    *(uint4*)(q_lds + r * KRB + cc * 16) = val;
+  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
+  const int P = p.page_size;
+  // Page id of this lane's key in the wave's first block.  Keys past the
+  // visible end clamp to the last visible key (their weight is 0 later), so
+  // every load below is unconditional.
+  auto page_of = [&](int blk) {
+    const int t = blk + lane;
+    const int tc = t < end_max ? t : end_max - 1;
+    return pt[tc / P];
+  };
+  int blk0 = sb + wave * 64;
+  int page_next = blk0 < end_max ? page_of(blk0) : 0;
+
+  // Query rows are wave-uniform: read through the constant address space
+  // they become scalar loads into SGPRs, and v_dot2 takes them as its scalar
+  // operand, so the broadcast costs neither LDS bandwidth nor VGPRs.  Rows
+  // past the group point at row 0 of the tile (their scores are masked).
+  const qconst_t* qrow[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int gr = tile * RT + r;
+    if (gr >= p.rows_total) gr = tile * RT;
+    const int j = gr / p.group, h = kvh * p.group + gr % p.group;
+    qrow[r] = (const qconst_t*)((const uint8_t*)p.q +
+                                ((((int64_t)b * p.q_len + j) * p.num_q_heads + h) * DK) * ES);
   }
-  __syncthreads();
 
   float m[RT], l[RT], acc[RT][VE];
 #pragma unroll
@@ -103,41 +140,93 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
 
   const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)kvh * p.ks_head * ES;
   const uint8_t* vbase = (const uint8_t*)p.v + (int64_t)kvh * p.vs_head * ES + x * (VU4 * 16);
-  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
-  const int P = p.page_size;
+  const int64_t ks_page16 = p.ks_page * ES / 16, ks_tok16 = p.ks_tok * ES / 16;
+  const int64_t vs_page16 = p.vs_page * ES / 16, vs_tok16 = p.vs_tok * ES / 16;
 
-  for (int blk = sb + wave * 64; blk < end_max; blk += NW * 64) {
+  for (int blk = blk0; blk < end_max; blk += NW * 64) {
+    // ---- page walk ----
     const int t = blk + lane;
-    const bool tv = t < end_max;
-    const int pg_idx = t / P;
-    const int page = tv ? pt[pg_idx] : 0;
-    const int slot = t - pg_idx * P;
+    const int tc = t < end_max ? t : end_max - 1;
+    const int page = page_next;
+    const int slot = tc - (tc / P) * P;
+    const uint32_t koff = (uint32_t)(page * ks_page16 + slot * ks_tok16);
+    const uint32_t voff = (uint32_t)(page * vs_page16 + slot * vs_tok16);
+    if (blk + NW * 64 < end_max) page_next = page_of(blk + NW * 64);
 
-    // ---- Q.K for key t ----
+    // ---- issue K (straight into the LDS tile), then V (16 rows per DPP row) ----
+    if constexpr (C::KLDS && C::RPI == 4) {
+      // Load i moves keys i, 16+i, 32+i, 48+i (one per DPP row); each row
+      // takes its key's offset by row_newbcast, no LDS round trip.
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        auto one = [&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          const uint32_t off = (uint32_t)row_bcast_i32<i>((int)koff);
+          lds_dma16(kbase + (uint64_t)off * 16 + x * 16, wave_lds + i * C::GP);
+        };
+        (one(std::integral_constant<int, I>{}), ...);
+      }(std::make_integer_sequence<int, 16>{});
+    } else if constexpr (C::KLDS) {
+      // Load i moves keys i*RPI .. i*RPI + RPI - 1 (offsets by ds_bpermute).
+      uint32_t offs[C::KINS];
+#pragma unroll
+      for (int i = 0; i < C::KINS; ++i) offs[i] = (uint32_t)__shfl((int)koff, i * C::RPI + lane / KCH);
+#pragma unroll
+      for (int i = 0; i < C::KINS; ++i)
+        lds_dma16(kbase + (uint64_t)offs[i] * 16 + (lane % KCH) * 16, wave_lds + i * C::GP);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 vv[16][VU4];
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      auto one = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const uint32_t off = (uint32_t)row_bcast_i32<i>((int)voff);
+        const uint8_t* vrow = vbase + (uint64_t)off * 16;
+#pragma unroll
+        for (int u = 0; u < VU4; ++u) vv[i][u] = *(const uint4*)(vrow + u * 16);
+      };
+      (one(std::integral_constant<int, I>{}), ...);
+    }(std::make_integer_sequence<int, 16>{});
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- Q.K, lane t = key t ----
+    // An opaque per-block offset keeps the compiler from hoisting every
+    // query chunk of every row out of the block loop at once.
+    uint32_t qoff = 0;
+    asm volatile("" : "+s"(qoff));
     float sc[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) sc[r] = 0.f;
-    if (tv) {
-      const uint8_t* krow = kbase + ((int64_t)page * p.ks_page + (int64_t)slot * p.ks_tok) * ES;
-#pragma unroll 8
-      for (int c = 0; c < KCH; ++c) {
-        const uint4 kc = *(const uint4*)(krow + c * 16);
+    auto dot_chunk = [&](const uint4 kc, int c) {
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          const uint4 qc = *(const uint4*)(q_lds + r * KRB + c * 16);
-          if constexpr (DTYPE == 0) {
-            sc[r] = fmaf(__builtin_bit_cast(float, qc.x), __builtin_bit_cast(float, kc.x), sc[r]);
-            sc[r] = fmaf(__builtin_bit_cast(float, qc.y), __builtin_bit_cast(float, kc.y), sc[r]);
-            sc[r] = fmaf(__builtin_bit_cast(float, qc.z), __builtin_bit_cast(float, kc.z), sc[r]);
-            sc[r] = fmaf(__builtin_bit_cast(float, qc.w), __builtin_bit_cast(float, kc.w), sc[r]);
-          } else {
-            sc[r] = dot2_bf16(qc.x, kc.x, sc[r]);
-            sc[r] = dot2_bf16(qc.y, kc.y, sc[r]);
-            sc[r] = dot2_bf16(qc.z, kc.z, sc[r]);
-            sc[r] = dot2_bf16(qc.w, kc.w, sc[r]);
-          }
+      for (int r = 0; r < RT; ++r) {
+        const qconst_t* qw = qrow[r] + (qoff + c) * 4;
+        const uint4 qc = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+        if constexpr (DTYPE == 0) {
+          sc[r] = fmaf(__builtin_bit_cast(float, qc.x), __builtin_bit_cast(float, kc.x), sc[r]);
+          sc[r] = fmaf(__builtin_bit_cast(float, qc.y), __builtin_bit_cast(float, kc.y), sc[r]);
+          sc[r] = fmaf(__builtin_bit_cast(float, qc.z), __builtin_bit_cast(float, kc.z), sc[r]);
+          sc[r] = fmaf(__builtin_bit_cast(float, qc.w), __builtin_bit_cast(float, kc.w), sc[r]);
+        } else {
+          sc[r] = dot2_bf16(qc.x, kc.x, sc[r]);
+          sc[r] = dot2_bf16(qc.y, kc.y, sc[r]);
+          sc[r] = dot2_bf16(qc.z, kc.z, sc[r]);
+          sc[r] = dot2_bf16(qc.w, kc.w, sc[r]);
         }
       }
+    };
+    if constexpr (C::KLDS) {
+      // K has landed once at most the V loads are outstanding.
+      wait_vmcnt<16 * VU4>();
+      // Where key `lane` sits in the tile (see the two load orders above).
+      const uint8_t* krow = C::RPI == 4 ? wave_lds + (lane & 15) * C::GP + (lane >> 4) * KRB
+                                        : wave_lds + (lane / C::RPI) * C::GP + (lane % C::RPI) * KRB;
+#pragma unroll 2
+      for (int c = 0; c < KCH; ++c) dot_chunk(*(const uint4*)(krow + c * 16), c);
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      const uint8_t* krow = kbase + (uint64_t)koff * 16;
+#pragma unroll 8
+      for (int c = 0; c < KCH; ++c) dot_chunk(*(const uint4*)(krow + c * 16), c);
     }
 
     // ---- online softmax, per 16-lane row ----
@@ -151,113 +240,135 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
       al[r] = mn == kNegInf ? 1.f : fast_exp2(m[r] - mn);
       changed |= al[r] != 1.f;
       pr[r] = sc[r] == kNegInf ? 0.f : fast_exp2(sc[r] - mn);
-      l[r] = l[r] * al[r] + pr[r];
       m[r] = mn;
     }
     if (__any(changed)) {
 #pragma unroll
-      for (int r = 0; r < RT; ++r)
+      for (int r = 0; r < RT; ++r) {
+        l[r] *= al[r];
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[r][e] *= al[r];
+      }
     }
 
-    // ---- P.V: row g accumulates keys blk + 16g + i ----
-    const int tg = blk + 16 * g;
-    auto pv_step = [&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      const int page_i = row_bcast_i32<i>(page);
-      const int slot_i = row_bcast_i32<i>(slot);
-      float pw[RT];
+    if constexpr (DTYPE == 0) {
+      // fp32: P.V with fp32 weights and FMAs.
 #pragma unroll
-      for (int r = 0; r < RT; ++r) pw[r] = row_bcast_f32<i>(pr[r]);
-      if (tg + i < end_max) {
-        const uint8_t* vrow = vbase + ((int64_t)page_i * p.vs_page + (int64_t)slot_i * p.vs_tok) * ES;
+      for (int r = 0; r < RT; ++r) l[r] += pr[r];
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        auto one = [&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          float pw[RT];
 #pragma unroll
-        for (int u = 0; u < VU4; ++u) {
-          const uint4 vv = *(const uint4*)(vrow + u * 16);
-          float vf[16 / ES];
-          if constexpr (DTYPE == 0) {
-            vf[0] = __builtin_bit_cast(float, vv.x);
-            vf[1] = __builtin_bit_cast(float, vv.y);
-            vf[2] = __builtin_bit_cast(float, vv.z);
-            vf[3] = __builtin_bit_cast(float, vv.w);
-          } else {
-            vf[0] = bf16_lo(vv.x); vf[1] = bf16_hi(vv.x);
-            vf[2] = bf16_lo(vv.y); vf[3] = bf16_hi(vv.y);
-            vf[4] = bf16_lo(vv.z); vf[5] = bf16_hi(vv.z);
-            vf[6] = bf16_lo(vv.w); vf[7] = bf16_hi(vv.w);
+          for (int r = 0; r < RT; ++r) pw[r] = row_bcast_f32<i>(pr[r]);
+#pragma unroll
+          for (int u = 0; u < VU4; ++u) {
+            const float vf[4] = {__builtin_bit_cast(float, vv[i][u].x), __builtin_bit_cast(float, vv[i][u].y),
+                                 __builtin_bit_cast(float, vv[i][u].z), __builtin_bit_cast(float, vv[i][u].w)};
+#pragma unroll
+            for (int r = 0; r < RT; ++r)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[r][u * 4 + e] = fmaf(pw[r], vf[e], acc[r][u * 4 + e]);
           }
+        };
+        (one(std::integral_constant<int, I>{}), ...);
+      }(std::make_integer_sequence<int, 16>{});
+    } else {
+      // bf16: weights of keys 2i and 2i+1 travel as one bf16 pair, V of the
+      // two keys is interleaved by v_perm, and v_dot2_f32_bf16 accumulates
+      // both keys in fp32.  The row sum keeps the fp32 weights: the
+      // log-sum-exp must hold to 1e-3, which bf16 weights (2^-9 relative
+      // each) cannot promise for short splits.
+      const bool odd = x & 1;
+      uint32_t pp[RT];
 #pragma unroll
-          for (int r = 0; r < RT; ++r)
-#pragma unroll
-            for (int e = 0; e < 16 / ES; ++e)
-              acc[r][u * (16 / ES) + e] = fmaf(pw[r], vf[e], acc[r][u * (16 / ES) + e]);
-        }
+      for (int r = 0; r < RT; ++r) {
+        const float other = dpp_f32<kDppQuadSwap1>(pr[r]);
+        pp[r] = pack_bf16x2(odd ? other : pr[r], odd ? pr[r] : other);
+        l[r] += pr[r];
       }
-    };
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      (pv_step(std::integral_constant<int, I>{}), ...);
-    }(std::make_integer_sequence<int, 16>{});
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        auto pair = [&](auto ic) {
+          constexpr int i = decltype(ic)::value;  // keys 2i, 2i+1 of the row
+          uint32_t pw[RT];
+#pragma unroll
+          for (int r = 0; r < RT; ++r) pw[r] = (uint32_t)row_bcast_i32<2 * i>((int)pp[r]);
+#pragma unroll
+          for (int u = 0; u < VU4; ++u) {
+            const uint32_t a[4] = {vv[2 * i][u].x, vv[2 * i][u].y, vv[2 * i][u].z, vv[2 * i][u].w};
+            const uint32_t c[4] = {vv[2 * i + 1][u].x, vv[2 * i + 1][u].y, vv[2 * i + 1][u].z,
+                                   vv[2 * i + 1][u].w};
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+              const uint32_t lo = __builtin_amdgcn_perm(c[w2], a[w2], 0x05040100u);  // dim 2w2
+              const uint32_t hi = __builtin_amdgcn_perm(c[w2], a[w2], 0x07060302u);  // dim 2w2+1
+#pragma unroll
+              for (int r = 0; r < RT; ++r) {
+                acc[r][u * 8 + 2 * w2] = dot2_bf16(pw[r], lo, acc[r][u * 8 + 2 * w2]);
+                acc[r][u * 8 + 2 * w2 + 1] = dot2_bf16(pw[r], hi, acc[r][u * 8 + 2 * w2 + 1]);
+              }
+            }
+          }
+        };
+        (pair(std::integral_constant<int, I>{}), ...);
+      }(std::make_integer_sequence<int, 8>{});
+    }
   }
 
-  // ---- merge the four 16-lane rows of the wave, then the waves ----
-  float mw[RT], lw[RT];
+  // ---- partial states of the 4*NW DPP rows into LDS, then one merge ----
+  // Each wave writes its four rows' states into its own region (its K tile
+  // is no longer read), so no barrier is needed before the writes.
+  float* pacc = (float*)wave_lds;                   // [4][RT][DV]
+  float* pml = pacc + 4 * RT * DV;                  // [4][RT] m, then [4][RT] l
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    float lt = row16_sum(l[r]);
-    float mx = fmaxf(m[r], __shfl_xor(m[r], 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float f = mx == kNegInf ? 0.f : fast_exp2(m[r] - mx);
-    lt *= f;
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = row16_sum(l[r]);
 #pragma unroll
-    for (int e = 0; e < VE; ++e) {
-      float a = acc[r][e] * f;
-      a += __shfl_xor(a, 16);
-      a += __shfl_xor(a, 32);
-      acc[r][e] = a;
-    }
-    mw[r] = mx;
-    lw[r] = lt;
-  }
-  if (g == 0) {
-#pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int e = 0; e < VE; ++e) comb_acc[wave][r][x * VE + e] = acc[r][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      comb_m[wave][r] = mw[r];
-      comb_l[wave][r] = lw[r];
+    for (int e = 0; e < VE; e += 4)
+      *(float4*)(pacc + (g * RT + r) * DV + x * VE + e) =
+          make_float4(acc[r][e], acc[r][e + 1], acc[r][e + 2], acc[r][e + 3]);
+    if (x == 0) {
+      pml[g * RT + r] = m[r];
+      pml[4 * RT + g * RT + r] = lt;
     }
   }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < RT * DV; idx += 64 * NW) {
-    const int r = idx / DV, d = idx % DV;
+  // Thread -> (row r, 4 consecutive dims); partials merged in a fixed order.
+  for (int idx = threadIdx.x; idx < RT * DV / 4; idx += 64 * NW) {
+    const int r = idx / (DV / 4), d = (idx % (DV / 4)) * 4;
     const int gr = tile * RT + r;
     if (gr >= p.rows_total) continue;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, comb_m[w][r]);
-    float o = 0.f, lse = kNegInf;
+    for (int k = 0; k < 4 * NW; ++k) {
+      const float* ml = (const float*)(smem + (k >> 2) * C::WAVE_B) + 4 * RT * DV;
+      M = fmaxf(M, ml[(k & 3) * RT + r]);
+    }
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lse = kNegInf;
     if (M != kNegInf) {
-      float den = 0.f, num = 0.f;
+      float den = 0.f;
+      float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float f = fast_exp2(comb_m[w][r] - M);
-        den += f * comb_l[w][r];
-        num += f * comb_acc[w][r][d];
+      for (int k = 0; k < 4 * NW; ++k) {
+        const float* base = (const float*)(smem + (k >> 2) * C::WAVE_B);
+        const float* ml = base + 4 * RT * DV;
+        const float f = fast_exp2(ml[(k & 3) * RT + r] - M);
+        den += f * ml[4 * RT + (k & 3) * RT + r];
+        const float4 a = *(const float4*)(base + ((k & 3) * RT + r) * DV + d);
+        num.x += f * a.x;
+        num.y += f * a.y;
+        num.z += f * a.z;
+        num.w += f * a.w;
       }
-      o = num / den;
+      const float inv = 1.f / den;
+      o = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
       lse = (M + __log2f(den)) * kLn2;
     }
     const int j = gr / p.group, h = kvh * p.group + gr % p.group;
     const int64_t row = ((int64_t)b * p.q_len + j) * p.num_q_heads + h;
-    p.o_part[(row * p.num_splits + s) * DV + d] = o;
+    *(float4*)(p.o_part + (row * p.num_splits + s) * DV + d) = o;
     if (d == 0) p.lse_part[row * p.num_splits + s] = lse;
   }
 }

@@ -5,8 +5,12 @@
 // One workgroup per (query row, Dv slice).  With few query rows (batch-1
 // decode) the host cuts the head dim into up to 8 slices so more CUs work;
 // each slice re-derives the row's max and weight sum on its own, so slices
-// never talk to each other and the result does not depend on the slicing.
-// Inside a workgroup, 256 threads = 16 split lanes x 16 four-float columns.
+// never talk to each other.  256 threads = 16 split lanes x 16 four-float
+// columns; split lane sl sums splits sl, sl + 16, ... and the lanes are then
+// added in lane order.  Every summation order depends on the split count
+// only, never on the slicing, so sliced and unsliced merges give the same
+// bits.  The partial-output loads are issued before the weights are known,
+// so the merge costs one memory round trip.
 #include "device_common.h"
 #include "launch.h"
 
@@ -19,6 +23,14 @@ constexpr int kThreads = 256;
 constexpr int kMaxSplitsLds = 4096;
 constexpr int kSL = 16;                     // split lanes
 constexpr int kColSlots = kThreads / kSL;   // float4 columns per pass
+constexpr int kChunk = 16;                  // splits per split lane held in registers
+
+// LDS-only workgroup barrier: wait for this wave's LDS traffic, then meet.
+// Global loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
+}
 
 template <int DTYPE>
 __global__ __launch_bounds__(kThreads) void stage2_kernel(Stage2Params p) {
@@ -29,56 +41,70 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(Stage2Params p) {
   const int row = blockIdx.x / p.tiles;
   const int tile = blockIdx.x % p.tiles;
   const int S = p.num_splits;
-  const int dvt = p.head_dim_v / p.tiles;  // slice width, a multiple of 4
-  const int cols = dvt / 4;                // float4 columns in the slice
+  const int Dv = p.head_dim_v;
+  const int dvt = Dv / p.tiles;  // slice width, a multiple of 4
+  const int cols = dvt / 4;      // float4 columns in the slice
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int cs = tid % kColSlots, sl = tid / kColSlots;
 
   const float* lse_row = p.lse_part + (int64_t)row * S;
+  const float* base = p.o_part + (int64_t)row * S * Dv + tile * dvt;
 
-  // Row max over the splits.
+  float4 ov[kChunk];
+  auto load_chunk = [&](int c0, int s0) {
+    const int col = c0 + cs;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const int s = s0 + sl + k * kSL;
+      ov[k] = (col < cols && s < S) ? *(const float4*)(base + (int64_t)s * Dv + col * 4)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  load_chunk(0, 0);
+
+  // Row max of the split log-sum-exps.
   float mx = kNegInf;
   for (int s = tid; s < S; s += kThreads) mx = fmaxf(mx, lse_row[s]);
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   if (lane == 0) red[wave] = mx;
-  __syncthreads();
+  lds_barrier();
   float M = red[0];
+#pragma unroll
   for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, red[w]);
-  __syncthreads();
+  lds_barrier();
 
-  // Weights exp(lse_s - M) and their sum, in a fixed order.
-  float den = 0.f;
-  if (M != kNegInf) {
-    for (int s = tid; s < S; s += kThreads) {
-      const float wgt = fast_exp2((lse_row[s] - M) * kLog2e);
-      w_lds[s] = wgt;
-    }
+  // Weights exp(lse_s - M) into LDS; their sum by a fixed-order tree.
+  float dl = 0.f;
+  for (int s = tid; s < S; s += kThreads) {
+    const float wgt = M == kNegInf ? 0.f : fast_exp2((lse_row[s] - M) * kLog2e);
+    w_lds[s] = wgt;
+    dl += wgt;
   }
-  __syncthreads();
-  if (M != kNegInf) {
-    for (int s = 0; s < S; ++s) den += w_lds[s];
-  }
+  for (int o = 32; o > 0; o >>= 1) dl += __shfl_xor(dl, o);
+  if (lane == 0) red[wave] = dl;
+  lds_barrier();
+  float den = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) den += red[w];
 
-  // Thread (sl, cs): split lane sl sums splits sl, sl + kSL, ...; the kSL
-  // lane sums are then added in lane order.  kSL does not depend on the
-  // slicing, so sliced and unsliced merges give the same bits.
-  const int cs = tid % kColSlots, sl = tid / kColSlots;
-  const float* base = p.o_part + (int64_t)row * S * p.head_dim_v + tile * dvt;
   for (int c0 = 0; c0 < cols; c0 += kColSlots) {
     const int col = c0 + cs;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M != kNegInf && col < cols) {
-      for (int s = sl; s < S; s += kSL) {
-        const float wgt = w_lds[s];
-        const float4 v = *(const float4*)(base + (int64_t)s * p.head_dim_v + col * 4);
-        a.x = fmaf(wgt, v.x, a.x);
-        a.y = fmaf(wgt, v.y, a.y);
-        a.z = fmaf(wgt, v.z, a.z);
-        a.w = fmaf(wgt, v.w, a.w);
+    for (int s0 = 0; s0 < S; s0 += kSL * kChunk) {
+      if (c0 != 0 || s0 != 0) load_chunk(c0, s0);
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) {
+        const int s = s0 + sl + k * kSL;
+        const float wgt = s < S ? w_lds[s] : 0.f;
+        a.x = fmaf(wgt, ov[k].x, a.x);
+        a.y = fmaf(wgt, ov[k].y, a.y);
+        a.z = fmaf(wgt, ov[k].z, a.z);
+        a.w = fmaf(wgt, ov[k].w, a.w);
       }
     }
     part[tid] = a;
-    __syncthreads();
+    lds_barrier();
     if (sl == 0 && col < cols) {
       float4 t = part[cs];
       for (int k = 1; k < kSL; ++k) {
@@ -90,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(Stage2Params p) {
         const float inv = 1.f / den;
         o = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
       }
-      const int64_t off = (int64_t)row * p.head_dim_v + tile * dvt + col * 4;
+      const int64_t off = (int64_t)row * Dv + tile * dvt + col * 4;
       if constexpr (DTYPE == 0) {
         *(float4*)((float*)p.out + off) = o;
       } else {
@@ -100,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(Stage2Params p) {
         *(uint2*)((uint16_t*)p.out + off) = pk;
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   if (p.lse && tile == 0 && tid == 0) p.lse[row] = M == kNegInf ? kNegInf : M + __logf(den);
 }
