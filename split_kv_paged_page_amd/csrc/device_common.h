@@ -25,15 +25,17 @@ constexpr int kDppRowMirror = 0x140;
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowNewBcast0 = 0x150;  // row_newbcast:n = 0x150 + n (gfx90a and later)
 
+// Every DPP pattern used here reads a valid lane for every lane, so the
+// "old" operand is never observed: mov_dpp leaves it undefined and saves the
+// zero-initialising move update_dpp would need.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                               0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
 }
 
 template <int CTRL>
 __device__ __forceinline__ int dpp_i32(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xf, 0xf, false);
 }
 
 // Value of lane N of this lane's 16-lane row, for every lane of the row.

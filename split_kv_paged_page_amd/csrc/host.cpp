@@ -51,6 +51,8 @@ attn_status check_desc(const attn_decode_desc* d) {
       d->num_pages < 1)
     return fail(ATTN_EINVAL, "head dims, page size, max_pages_per_req and num_pages must be >= 1");
   if (d->dtype != ATTN_F32 && d->dtype != ATTN_BF16) return fail(ATTN_EINVAL, "unknown dtype %d", d->dtype);
+  if (d->page_size & (d->page_size - 1))
+    return fail(ATTN_EUNSUPPORTED, "page_size %d is not a power of two", d->page_size);
   if (d->causal != 0 && d->causal != 1) return fail(ATTN_EINVAL, "causal must be 0 or 1");
   if (d->v_aliases_k != 0 && d->v_aliases_k != 1) return fail(ATTN_EINVAL, "v_aliases_k must be 0 or 1");
   if (d->reserved != 0) return fail(ATTN_EINVAL, "reserved must be 0");
@@ -148,6 +150,8 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   p.num_kv_heads = d.num_kv_heads;
   p.group = d.num_q_heads / d.num_kv_heads;
   p.page_size = d.page_size;
+  p.page_shift = 0;
+  while ((1 << p.page_shift) < d.page_size) ++p.page_shift;
   p.max_pages = d.max_pages_per_req;
   p.causal = d.causal;
   p.num_splits = S;
@@ -165,7 +169,10 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   p.vs_page = d.v_stride_page;
   p.vs_head = d.v_stride_head;
   p.vs_tok = d.v_stride_tok;
-  hipError_t e = splitkv::launch_stage1_valu(p, d.dtype, d.head_dim_qk, d.head_dim_v, st);
+  // Query rows of one workgroup are contiguous in q when they all belong to
+  // one query position: every tile then lies inside one GQA group.
+  const bool q_contig = (p.group % plan->rows_per_wg) == 0 || (d.q_len == 1 && p.rows_total == plan->rows_per_wg);
+  hipError_t e = splitkv::launch_stage1_valu(p, d.dtype, d.head_dim_qk, d.head_dim_v, q_contig, st);
   if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
   return ATTN_OK;
 }

@@ -17,6 +17,7 @@ struct Stage1Params {
   float scale_log2;       // scale * log2(e): scores are kept in base-2 units
   int32_t batch, q_len, num_q_heads, num_kv_heads, group;
   int32_t page_size, max_pages, causal;
+  int32_t page_shift;     // log2(page_size)
   int32_t num_splits, split_align;
   int32_t rows_total;     // query rows per KV head = group * q_len
   int32_t rows_per_wg, head_tiles;
@@ -39,7 +40,7 @@ struct Stage2Params {
 
 // Stage-1 launchers; return false when no kernel exists for the shape.
 bool stage1_valu_supported(int dtype, int dk, int dv, int rows_per_wg);
-hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, hipStream_t s);
+hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, bool q_contig, hipStream_t s);
 
 bool stage2_supported(int dtype, int dv, int tiles);
 hipError_t launch_stage2(const Stage2Params& p, int dtype, hipStream_t s);

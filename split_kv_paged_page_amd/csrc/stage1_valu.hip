@@ -61,7 +61,7 @@ struct Cfg {
   static_assert(RT * VE <= 128, "accumulator budget");
 };
 
-template <int DTYPE, int DK, int DV, int RT, int NW>
+template <int DTYPE, int DK, int DV, int RT, int NW, bool QC>
 __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
   using C = Cfg<DTYPE, DK, DV, RT, NW>;
   constexpr int ES = C::ES, KRB = C::KRB, KCH = C::KCH, VU4 = C::VU4, VE = C::VE;
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
   __shared__ __align__(16) uint8_t smem[C::SMEM];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
   const int g = lane >> 4;
   const int x = lane & 15;
   uint8_t* wave_lds = smem + wave * C::WAVE_B;
@@ -107,10 +107,11 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
   // Page id of this lane's key in the wave's first block.  Keys past the
   // visible end clamp to the last visible key (their weight is 0 later), so
   // every load below is unconditional.
+  const int psh = p.page_shift;  // page sizes are powers of two
   auto page_of = [&](int blk) {
     const int t = blk + lane;
     const int tc = t < end_max ? t : end_max - 1;
-    return pt[tc / P];
+    return pt[tc >> psh];
   };
   int blk0 = sb + wave * 64;
   int page_next = blk0 < end_max ? page_of(blk0) : 0;
@@ -120,13 +121,24 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
   // operand, so the broadcast costs neither LDS bandwidth nor VGPRs.  Rows
   // past the group point at row 0 of the tile (their scores are masked).
   const qconst_t* qrow[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    int gr = tile * RT + r;
-    if (gr >= p.rows_total) gr = tile * RT;
+  if constexpr (QC) {
+    // The tile's rows are consecutive query heads of one query position:
+    // one base and constant offsets (immediate offsets of s_load).
+    const int gr = tile * RT;
     const int j = gr / p.group, h = kvh * p.group + gr % p.group;
-    qrow[r] = (const qconst_t*)((const uint8_t*)p.q +
-                                ((((int64_t)b * p.q_len + j) * p.num_q_heads + h) * DK) * ES);
+    const qconst_t* q0 = (const qconst_t*)((const uint8_t*)p.q +
+                                           ((((int64_t)b * p.q_len + j) * p.num_q_heads + h) * DK) * ES);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) qrow[r] = q0 + r * (KRB / 4);
+  } else {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      int gr = tile * RT + r;
+      if (gr >= p.rows_total) gr = tile * RT;
+      const int j = gr / p.group, h = kvh * p.group + gr % p.group;
+      qrow[r] = (const qconst_t*)((const uint8_t*)p.q +
+                                  ((((int64_t)b * p.q_len + j) * p.num_q_heads + h) * DK) * ES);
+    }
   }
 
   float m[RT], l[RT], acc[RT][VE];
@@ -148,7 +160,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
     const int t = blk + lane;
     const int tc = t < end_max ? t : end_max - 1;
     const int page = page_next;
-    const int slot = tc - (tc / P) * P;
+    const int slot = tc & (P - 1);
     const uint32_t koff = (uint32_t)(page * ks_page16 + slot * ks_tok16);
     const uint32_t voff = (uint32_t)(page * vs_page16 + slot * vs_tok16);
     if (blk + NW * 64 < end_max) page_next = page_of(blk + NW * 64);
@@ -238,7 +250,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
       const float bm = row16_max(sc[r]);
       const float mn = fmaxf(m[r], bm);
       al[r] = mn == kNegInf ? 1.f : fast_exp2(m[r] - mn);
-      changed |= al[r] != 1.f;
+      changed |= al[r] != 1.f && m[r] != kNegInf;  // a row with no key yet has nothing to rescale
       pr[r] = sc[r] == kNegInf ? 0.f : fast_exp2(sc[r] - mn);
       m[r] = mn;
     }
@@ -373,29 +385,22 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
   }
 }
 
-template <int DTYPE, int DK, int DV, int RT>
-constexpr auto kernel_ptr() {
-  return &stage1_valu_kernel<DTYPE, DK, DV, RT, 4>;
-}
-
 struct Entry {
   int dtype, dk, dv, rt;
-  void (*fn)(Stage1Params);
+  void (*fn[2])(Stage1Params);  // [q rows contiguous]
 };
 
+template <int DTYPE, int DK, int DV, int RT>
+constexpr Entry entry() {
+  return {DTYPE, DK, DV, RT, {&stage1_valu_kernel<DTYPE, DK, DV, RT, 4, false>,
+                              &stage1_valu_kernel<DTYPE, DK, DV, RT, 4, true>}};
+}
+
 constexpr Entry kTable[] = {
-    {0, 64, 64, 4, kernel_ptr<0, 64, 64, 4>()},
-    {0, 64, 64, 8, kernel_ptr<0, 64, 64, 8>()},
-    {0, 64, 64, 16, kernel_ptr<0, 64, 64, 16>()},
-    {0, 128, 128, 4, kernel_ptr<0, 128, 128, 4>()},
-    {0, 128, 128, 8, kernel_ptr<0, 128, 128, 8>()},
-    {0, 128, 128, 16, kernel_ptr<0, 128, 128, 16>()},
-    {1, 128, 128, 4, kernel_ptr<1, 128, 128, 4>()},
-    {1, 128, 128, 8, kernel_ptr<1, 128, 128, 8>()},
-    {1, 128, 128, 16, kernel_ptr<1, 128, 128, 16>()},
-    {1, 256, 256, 4, kernel_ptr<1, 256, 256, 4>()},
-    {1, 256, 256, 8, kernel_ptr<1, 256, 256, 8>()},
-    {1, 576, 512, 4, kernel_ptr<1, 576, 512, 4>()},
+    entry<0, 64, 64, 4>(),   entry<0, 64, 64, 8>(),   entry<0, 64, 64, 16>(),
+    entry<0, 128, 128, 4>(), entry<0, 128, 128, 8>(), entry<0, 128, 128, 16>(),
+    entry<1, 128, 128, 4>(), entry<1, 128, 128, 8>(), entry<1, 128, 128, 16>(),
+    entry<1, 256, 256, 4>(), entry<1, 256, 256, 8>(), entry<1, 576, 512, 4>(),
 };
 
 const Entry* find(int dtype, int dk, int dv, int rt) {
@@ -410,10 +415,10 @@ bool stage1_valu_supported(int dtype, int dk, int dv, int rows_per_wg) {
   return find(dtype, dk, dv, rows_per_wg) != nullptr;
 }
 
-hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, hipStream_t st) {
+hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, bool q_contig, hipStream_t st) {
   const Entry* e = find(dtype, dk, dv, p.rows_per_wg);
   if (!e) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(e->fn, dim3(p.num_wgs), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(e->fn[q_contig ? 1 : 0], dim3(p.num_wgs), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

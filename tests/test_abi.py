@@ -146,6 +146,12 @@ def test_plan_rejects(mutate, status):
     assert sk.attn_decode_last_error()
 
 
+def test_plan_rejects_page_size_not_power_of_two():
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_plan(desc(P=24, maxp=100), 1024, 0)
+    assert ei.value.status == sk.ATTN_EUNSUPPORTED
+
+
 def test_plan_rejects_misaligned_stride():
     d = desc()
     d.k_stride_tok = 129          # 258-byte rows break 16-byte alignment
