@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsplitkv.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["host.cpp", "stage1_valu.hip", "stage2.hip"]
+SOURCES = ["host.cpp", "stage1_valu.hip", "stage1_mfma.hip", "stage2.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -172,7 +172,9 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   // Query rows of one workgroup are contiguous in q when they all belong to
   // one query position: every tile then lies inside one GQA group.
   const bool q_contig = (p.group % plan->rows_per_wg) == 0 || (d.q_len == 1 && p.rows_total == plan->rows_per_wg);
-  hipError_t e = splitkv::launch_stage1_valu(p, d.dtype, d.head_dim_qk, d.head_dim_v, q_contig, st);
+  hipError_t e = plan->variant == ATTN_VARIANT_MFMA
+                     ? splitkv::launch_stage1_mfma(p, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0, st)
+                     : splitkv::launch_stage1_valu(p, d.dtype, d.head_dim_qk, d.head_dim_v, q_contig, st);
   if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
   return ATTN_OK;
 }
@@ -223,20 +225,26 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
 
   const attn_decode_desc& d = *desc;
   const int rows = (d.num_q_heads / d.num_kv_heads) * d.q_len;
-  const int rt = pick_rows_per_wg(d.dtype, d.head_dim_qk, d.head_dim_v, rows);
-  if (!rt)
-    return fail(ATTN_EUNSUPPORTED, "no stage-1 kernel for dtype %d, head dims %d/%d", d.dtype, d.head_dim_qk,
-                d.head_dim_v);
-
   attn_decode_plan_t p{};
   p.desc = d;
   p.max_context_len = max_context_len;
   p.split_align = kSplitAlign;
-  p.variant = ATTN_VARIANT_VALU;
-  p.rows_per_wg = rt;
-  p.head_tiles = (rows + rt - 1) / rt;
   p.flags = flags;
   p.xcd_remap = (flags & ATTN_PLAN_NO_XCD_REMAP) ? 0 : 1;
+  // Matrix cores only where 16 or more query rows share a KV head: below
+  // that Q.K and P.V are not dense enough for a 16-row MFMA tile.
+  if (rows >= 16 && splitkv::stage1_mfma_supported(d.dtype, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0)) {
+    p.variant = ATTN_VARIANT_MFMA;
+    p.rows_per_wg = 16;
+  } else {
+    const int rt = pick_rows_per_wg(d.dtype, d.head_dim_qk, d.head_dim_v, rows);
+    if (!rt)
+      return fail(ATTN_EUNSUPPORTED, "no stage-1 kernel for dtype %d, head dims %d/%d", d.dtype, d.head_dim_qk,
+                  d.head_dim_v);
+    p.variant = ATTN_VARIANT_VALU;
+    p.rows_per_wg = rt;
+  }
+  p.head_tiles = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
 
   // Split count.  The aiter PR's launcher gives each request about 256 /
   // batch splits so that the 256 CUs stay busy (Motivation; Test Result
