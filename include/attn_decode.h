@@ -136,7 +136,9 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
 
 /*
  * Full decode: stage 1 (partials into the workspace) then stage 2 (merge into
- * out and, when lse is non-null, lse), both enqueued on `stream`.
+ * out and, when lse is non-null, lse), both enqueued on `stream`.  With one
+ * split, stage 1 writes out and lse itself (the same bits a merge of one
+ * split gives) and the workspace is not touched.
  * num_splits = 0 uses plan->num_splits; any value in [1, plan->max_splits]
  * is allowed (results agree up to float rounding).  workspace_bytes must be
  * at least the size attn_decode_workspace_layout reports for that split

@@ -99,6 +99,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
 }
 
+// Four consecutive outputs in the output dtype (0: fp32, 1: bf16 nearest-even).
+__device__ __forceinline__ void store_out4(void* out, int dtype, int64_t off, float4 o) {
+  if (dtype == 0) {
+    *(float4*)((float*)out + off) = o;
+  } else {
+    uint2 pk;
+    pk.x = pack_bf16x2(o.x, o.y);
+    pk.y = pack_bf16x2(o.z, o.w);
+    *(uint2*)((uint16_t*)out + off) = pk;
+  }
+}
+
 // Split rule: split s of S over ctx keys, chunk = A * ceil(ceil(ctx / S) / A).
 __device__ __forceinline__ void split_range(int ctx, int S, int A, int s, int& beg, int& end) {
   int per = (ctx + S - 1) / S;

@@ -123,7 +123,8 @@ attn_status resolve_splits(const attn_decode_plan_t* p, int32_t num_splits, int*
 
 attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q, const void* k,
                            const void* v, const int32_t* pt, const int32_t* ctx, float scale,
-                           void* ws, int64_t ws_bytes, hipStream_t st) {
+                           void* ws, int64_t ws_bytes, hipStream_t st, void* out = nullptr,
+                           float* lse_out = nullptr) {
   const attn_decode_desc& d = plan->desc;
   if (!q || !k || !v || !pt || !ctx || !ws) return fail(ATTN_EINVAL, "a device pointer is null");
   if (d.v_aliases_k && v != k) return fail(ATTN_EINVAL, "aliased V: v_cache must equal k_cache");
@@ -136,6 +137,8 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
     return fail(ATTN_EWORKSPACE, "workspace of %lld bytes is below the %lld needed", (long long)ws_bytes,
                 (long long)need);
   splitkv::Stage1Params p{};
+  p.out = out;
+  p.lse_out = lse_out;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -341,6 +344,10 @@ attn_status attn_decode_run(const attn_decode_plan_t* plan, const void* q, const
   attn_status st = resolve_splits(plan, num_splits, &S);
   if (st != ATTN_OK) return st;
   if (!out) return fail(ATTN_EINVAL, "out is null");
+  if ((uintptr_t)out % 16 || (uintptr_t)lse % 4) return fail(ATTN_EINVAL, "out must be 16-byte aligned");
+  if (S == 1)  // one split: stage 1 writes the final output itself
+    return enqueue_stage1(plan, S, q, k_cache, v_cache, page_table, context_lens, scale, workspace,
+                          workspace_bytes, (hipStream_t)stream, out, lse);
   st = enqueue_stage1(plan, S, q, k_cache, v_cache, page_table, context_lens, scale, workspace,
                       workspace_bytes, (hipStream_t)stream);
   if (st != ATTN_OK) return st;

@@ -25,6 +25,10 @@ struct Stage1Params {
   int32_t num_wgs;        // S * B * Hkv * head_tiles
   int64_t ks_page, ks_head, ks_tok;   // elements
   int64_t vs_page, vs_head, vs_tok;
+  // Single split: write the final output (q dtype) and log-sum-exp directly
+  // instead of partials (identical bits to merging one split).
+  void* out;              // null: write partials
+  float* lse_out;         // optional with out
 };
 
 struct Stage2Params {

@@ -380,8 +380,13 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
     }
     const int j = gr / p.group, h = kvh * p.group + gr % p.group;
     const int64_t row = ((int64_t)b * p.q_len + j) * p.num_q_heads + h;
-    *(float4*)(p.o_part + (row * p.num_splits + s) * DV + d) = o;
-    if (d == 0) p.lse_part[row * p.num_splits + s] = lse;
+    if (p.out) {
+      store_out4(p.out, DTYPE, row * DV + d, o);
+      if (d == 0 && p.lse_out) p.lse_out[row] = lse;
+    } else {
+      *(float4*)(p.o_part + (row * p.num_splits + s) * DV + d) = o;
+      if (d == 0) p.lse_part[row * p.num_splits + s] = lse;
+    }
   }
 }
 

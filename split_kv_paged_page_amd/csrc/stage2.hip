@@ -5,12 +5,13 @@
 // One workgroup per (query row, Dv slice).  With few query rows (batch-1
 // decode) the host cuts the head dim into up to 8 slices so more CUs work;
 // each slice re-derives the row's max and weight sum on its own, so slices
-// never talk to each other.  256 threads = 16 split lanes x 16 four-float
-// columns; split lane sl sums splits sl, sl + 16, ... and the lanes are then
-// added in lane order.  Every summation order depends on the split count
-// only, never on the slicing, so sliced and unsliced merges give the same
-// bits.  The partial-output loads are issued before the weights are known,
-// so the merge costs one memory round trip.
+// never talk to each other.  256 threads = SL split lanes x (256 / SL)
+// four-float columns, SL = the largest power of two <= min(S, 16); split
+// lane sl sums splits sl, sl + SL, ... and the lanes are then added in lane
+// order.  Every summation order depends on the split count only, never on
+// the slicing, so sliced and unsliced merges give the same bits.  The
+// partial-output loads are issued before the weights are known, so the
+// merge costs one memory round trip.
 #include "device_common.h"
 #include "launch.h"
 
@@ -21,8 +22,6 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kThreads = 256;
 constexpr int kMaxSplitsLds = 4096;
-constexpr int kSL = 16;                     // split lanes
-constexpr int kColSlots = kThreads / kSL;   // float4 columns per pass
 constexpr int kChunk = 16;                  // splits per split lane held in registers
 
 // LDS-only workgroup barrier: wait for this wave's LDS traffic, then meet.
@@ -46,6 +45,9 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(Stage2Params p) {
   const int cols = dvt / 4;      // float4 columns in the slice
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  int kSL = 1;
+  while (kSL < 16 && kSL * 2 <= S) kSL *= 2;
+  const int kColSlots = kThreads / kSL;
   const int cs = tid % kColSlots, sl = tid / kColSlots;
 
   const float* lse_row = p.lse_part + (int64_t)row * S;
@@ -116,15 +118,7 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(Stage2Params p) {
         const float inv = 1.f / den;
         o = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
       }
-      const int64_t off = (int64_t)row * Dv + tile * dvt + col * 4;
-      if constexpr (DTYPE == 0) {
-        *(float4*)((float*)p.out + off) = o;
-      } else {
-        uint2 pk;
-        pk.x = pack_bf16x2(o.x, o.y);
-        pk.y = pack_bf16x2(o.z, o.w);
-        *(uint2*)((uint16_t*)p.out + off) = pk;
-      }
+      store_out4(p.out, DTYPE, (int64_t)row * Dv + tile * dvt + col * 4, o);
     }
     lds_barrier();
   }

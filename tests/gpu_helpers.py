@@ -51,6 +51,7 @@ class Decode:
         self.out = torch.empty((w.batch, w.q_len, w.num_q_heads, w.head_dim_v), dtype=self.dtype,
                                device="cuda")
         self.lse = torch.empty((w.batch, w.q_len, w.num_q_heads), dtype=torch.float32, device="cuda")
+        self.partials_written = False
 
     @property
     def v(self):
@@ -66,6 +67,8 @@ class Decode:
         if poison:
             self.poison()
         t = self.t
+        # one split: stage 1 writes the output directly, no partials
+        self.partials_written = (num_splits or self.S) > 1
         sk.attn_decode_run(self.plan, t["q"], t["k_cache"], self.v, t["page_table"], t["context_lens"],
                            float(self.inp.scale), num_splits or self.S, self.out, self.lse, self.ws)
         torch.cuda.synchronize()
@@ -77,6 +80,7 @@ class Decode:
         sk.attn_decode_partials(self.plan, t["q"], t["k_cache"], self.v, t["page_table"], t["context_lens"],
                                 float(self.inp.scale), num_splits or self.S, self.ws)
         torch.cuda.synchronize()
+        self.partials_written = True
 
     def merge(self, num_splits=None):
         import torch
