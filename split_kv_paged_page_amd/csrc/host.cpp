@@ -176,7 +176,8 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   // one query position: every tile then lies inside one GQA group.
   const bool q_contig = (p.group % plan->rows_per_wg) == 0 || (d.q_len == 1 && p.rows_total == plan->rows_per_wg);
   hipError_t e = plan->variant == ATTN_VARIANT_MFMA
-                     ? splitkv::launch_stage1_mfma(p, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0, st)
+                     ? splitkv::launch_stage1_mfma(p, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0,
+                                                   plan->rows_per_wg / 16, st)
                      : splitkv::launch_stage1_valu(p, d.dtype, d.head_dim_qk, d.head_dim_v, q_contig, st);
   if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
   return ATTN_OK;
@@ -238,7 +239,7 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
   // that Q.K and P.V are not dense enough for a 16-row MFMA tile.
   if (rows >= 16 && splitkv::stage1_mfma_supported(d.dtype, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0)) {
     p.variant = ATTN_VARIANT_MFMA;
-    p.rows_per_wg = 16;
+    p.rows_per_wg = 16 * splitkv::stage1_mfma_row_tiles(d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0, rows);
   } else {
     const int rt = pick_rows_per_wg(d.dtype, d.head_dim_qk, d.head_dim_v, rows);
     if (!rt)
@@ -262,8 +263,11 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
     S = kNumCu / d.batch;
     if (S < 1) S = 1;
   } else {
+    // VALU workgroups fit two per CU; MFMA workgroups (large LDS tiles, a
+    // full register file per wave) one per CU: aim for one full round.
     const int per_split = d.batch * d.num_kv_heads * p.head_tiles;
-    S = (2 * kNumCu) / per_split;
+    const int target = p.variant == ATTN_VARIANT_MFMA ? kNumCu : 2 * kNumCu;
+    S = target / per_split;
     if (S > blocks) S = blocks;
     if (S < 1) S = 1;
   }

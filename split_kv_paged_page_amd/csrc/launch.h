@@ -47,7 +47,9 @@ bool stage1_valu_supported(int dtype, int dk, int dv, int rows_per_wg);
 hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, bool q_contig, hipStream_t s);
 
 bool stage1_mfma_supported(int dtype, int dk, int dv, bool v_aliases_k);
-hipError_t launch_stage1_mfma(const Stage1Params& p, int dk, int dv, bool v_aliases_k, hipStream_t s);
+int stage1_mfma_row_tiles(int dk, int dv, bool v_aliases_k, int rows);
+hipError_t launch_stage1_mfma(const Stage1Params& p, int dk, int dv, bool v_aliases_k, int row_tiles,
+                              hipStream_t s);
 
 bool stage2_supported(int dtype, int dv, int tiles);
 hipError_t launch_stage2(const Stage2Params& p, int dtype, hipStream_t s);

@@ -3,9 +3,14 @@
 // "[Gluon][MLA] Deeper async-copy pipeline in the bh16 stage-1 decode loop",
 // bh16 / bh64 regimes) or a wide GQA group with draft tokens.
 //
-// Each wave owns 16 query rows and walks 32-key blocks of its split; NW waves
-// of a workgroup take the blocks in turn with their own running max / sum /
-// accumulators and merge at the end.  Per block:
+// Each wave owns 16 query rows.  A workgroup has RW x KW waves: RW 16-row
+// tiles that share each K block through LDS (double-buffered, one barrier
+// per block; the next block's loads overlap the current block's compute) and
+// KW key streams that take the split's 32-key blocks in turn with their own
+// running max / sum / accumulators, merged at the end.  One tile and four
+// streams suit 16 rows per KV head; four tiles and one stream suit 64 or
+// more (the wide MLA shape reads each K block once per 64 rows).
+// Per block:
 //   * page walk: lane k < 32 looks up key k's page; keys past the visible end
 //     clamp to the last visible key (weight 0 later);
 //   * the block's K rows (and V rows when V is a separate cache) go straight
@@ -42,8 +47,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
-template <int DK, int DV, bool VALIAS, int NW>
+template <int DK, int DV, bool VALIAS, int RW, int KW>
 struct MCfg {
+  static constexpr int NW = RW * KW;               // waves: RW row tiles x KW key streams
+  static constexpr int NBUF = RW > 1 ? 4 : 1;      // shared tiles: a ring of 4 (3 blocks in flight)
   static constexpr int KCH = DK * 2 / 16;          // 16-byte chunks of a K row
   static constexpr int VCH = DV * 2 / 16;          // 16-byte chunks of a V row
   static constexpr int KK = DK / 32;               // Q.K MFMA steps
@@ -52,28 +59,99 @@ struct MCfg {
   static constexpr int VINS = VALIAS ? 0 : VCH / 2;
   static constexpr int KTILE = KCH * 32 * 16;      // bytes
   static constexpr int VTILE = VALIAS ? 0 : VCH * 32 * 16;
-  static constexpr int TILE = KTILE + VTILE;
+  static constexpr int TILE = ((KTILE + VTILE) + 255) / 256 * 256;
+  static constexpr int TILES = KW * NBUF * TILE;
+  static constexpr int PIDS = RW > 1 ? NW * NBUF * 256 : 0;  // per-wave page-id ring (shared tiles only)
   static constexpr int PART = 16 * DV * 4 + 2 * 16 * 4;  // merge state: acc [16][DV], m[16], l[16]
-  static constexpr int WAVE_B = ((TILE > PART ? TILE : PART) + 255) / 256 * 256;
-  static constexpr int SMEM = NW * WAVE_B;
+  static constexpr int PARTS = KW > 1 ? NW * PART : 0;   // only key streams need merging
+  static constexpr int SMEM = TILES + PIDS > PARTS ? TILES + PIDS : PARTS;
   static_assert(KCH % 4 == 0 && VCH % 4 == 0, "row sizes");
   static_assert(!VALIAS || DV <= DK, "aliased V");
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  static_assert(KINS % RW == 0 && VINS % RW == 0, "DMA instructions split evenly over the row tiles");
+  static_assert(RW == 1 || KW == 1, "shared tiles carry one key stream");
+  static constexpr int MINE = RW > 1 ? (KINS + VINS) / RW : 0;  // DMA instructions per wave per block
 };
 
 // 16-byte slot of chunk c of key k (k < 32) in a tile.
 __device__ __forceinline__ int tile_slot(int k, int c) { return (c >> 2) * 128 + k * 4 + ((c & 3) ^ ((k >> 2) & 3)); }
 
-template <int DK, int DV, bool VALIAS, int NW>
-__global__ __launch_bounds__(64 * NW) void stage1_mfma_kernel(Stage1Params p) {
-  using C = MCfg<DK, DV, VALIAS, NW>;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kLaK = 2;  // Q.K read steps in flight ahead of the MFMA
+constexpr int kLaV = 3;  // P.V read steps in flight ahead of the MFMA
+constexpr float kLazyLog2 = 8.f;  // reference-max slack (log2 units) before a rescale
+
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ptr;
+}
+
+// The tile reads are written as inline assembly.  A tile is filled by
+// global_load_lds, and the compiler, which cannot tell one tile from
+// another, would otherwise make every LDS read wait for all of those loads,
+// including the ones that fill the next tiles; the kernel orders the tiles
+// itself (vmcnt wait + barrier per block).  The reads are then invisible to
+// the compiler's counters, so each result passes through lds_wait2, which
+// waits until at most N LDS operations are outstanding and ties the
+// registers to the wait.  Other LDS or scalar-memory operations in flight
+// only make the wait stricter.
+template <int OFF>
+__device__ __forceinline__ void lds_read2_b128(i32x4_t& r0, i32x4_t& r1, uint32_t a0, uint32_t a1) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  asm volatile("ds_read_b128 %0, %2 offset:%4\n\tds_read_b128 %1, %3 offset:%4"
+               : "=&v"(r0), "=&v"(r1)
+               : "v"(a0), "v"(a1), "i"(OFF));
+}
+
+template <int OFF>
+__device__ __forceinline__ void lds_read2_tr16(i16x4_t& r0, i16x4_t& r1, uint32_t a0, uint32_t a1) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%4\n\tds_read_b64_tr_b16 %1, %3 offset:%4"
+               : "=&v"(r0), "=&v"(r1)
+               : "v"(a0), "v"(a1), "i"(OFF));
+}
+
+// Workgroup barrier for the shared tile ring.  Every wave has already
+// waited for its own DMA of the block being published (vmcnt) and for its
+// own reads of the tile being recycled (lds_wait2 down to 0), so only the
+// meeting is needed; a __syncthreads fence would also wait for the DMAs
+// still filling the next tiles.  The memory clobber keeps the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int OFF>
+__device__ __forceinline__ int lds_read_b32(uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  int r;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
+  return r;
+}
+
+template <int N, typename T>
+__device__ __forceinline__ void lds_wait1(T& r0) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r0) : "i"(N));
+}
+
+template <int N, typename T>
+__device__ __forceinline__ void lds_wait2(T& r0, T& r1) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r0), "+v"(r1) : "i"(N));
+}
+
+template <int DK, int DV, bool VALIAS, int RW, int KW>
+__global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params p) {
+  using C = MCfg<DK, DV, VALIAS, RW, KW>;
   __shared__ __align__(256) uint8_t smem[C::SMEM];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4;   // lane group
-  const int n = lane & 15;   // query row of this lane in the MFMA output
-  uint8_t* ktile = smem + wave * C::WAVE_B;
-  uint8_t* vtile = VALIAS ? ktile : ktile + C::KTILE;
+  const int rw = wave % RW;   // row tile of this wave
+  const int kw = wave / RW;   // key stream of this wave
+  const int g = lane >> 4;    // lane group
+  const int n = lane & 15;    // query row of this lane in the MFMA output
+  auto tile_k = [&](int buf) { return smem + (kw * C::NBUF + buf) * C::TILE; };
+  auto tile_v = [&](int buf) { return VALIAS ? tile_k(buf) : tile_k(buf) + C::KTILE; };
 
   int lid = logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap);
   const int tile = lid % p.head_tiles;
@@ -87,8 +165,8 @@ __global__ __launch_bounds__(64 * NW) void stage1_mfma_kernel(Stage1Params p) {
   int sb, se;
   split_range(L, p.num_splits, p.split_align, s, sb, se);
 
-  // This lane's query row (of the tile's 16) and its visible end.
-  const int gr = tile * 16 + n;
+  // This lane's query row and its visible end.
+  const int gr = (tile * RW + rw) * 16 + n;
   const bool row_ok = gr < p.rows_total;
   int row_end = sb;
   if (row_ok) {
@@ -97,27 +175,36 @@ __global__ __launch_bounds__(64 * NW) void stage1_mfma_kernel(Stage1Params p) {
     row_end = nv < se ? nv : se;
     if (row_end < sb) row_end = sb;
   }
-  // The workgroup's last visible key: the largest row end over the tile
-  // (rows of one tile differ only with causal drafts).
-  int end_max = row_end;
-  for (int o = 8; o > 0; o >>= 1) end_max = max(end_max, __shfl_xor(end_max, o));
-  end_max = __builtin_amdgcn_readfirstlane(end_max);
+  // The workgroup's last visible key over all its rows (rows differ only with
+  // causal drafts; every row of a workgroup belongs to one request).
+  const int first_row = tile * RW * 16;
+  int last_row = first_row + RW * 16 - 1;
+  if (last_row >= p.rows_total) last_row = p.rows_total - 1;
+  int end_max = sb;
+  {
+    const int j = last_row / p.group;
+    const int nv = p.causal ? L - p.q_len + 1 + j : L;
+    end_max = nv < se ? nv : se;
+    if (end_max < sb) end_max = sb;
+  }
 
   const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
   const int psh = p.page_shift, P = p.page_size;
-  const int blk0 = sb + wave * 32;
+  // Stream kw takes blocks it = 0, 1, ... at keys sb + (kw + it*KW)*32.  All
+  // streams run the same trip count so shared-tile barriers stay uniform.
+  const int nit = (end_max - sb + 32 * KW - 1) / (32 * KW);
+  auto blk_of = [&](int it) { return sb + (kw + it * KW) * 32; };
   auto page_of = [&](int blk) {
     const int t = blk + (lane & 31);
     const int tc = t < end_max ? t : end_max - 1;
     return pt[tc >> psh];
   };
-  int page_next = blk0 < end_max ? page_of(blk0) : 0;
 
   // Query rows as the B operand of S^T = K Q^T: lane l holds
   // q[row n][kk*32 + g*8 .. +7] for every kk (rows past the group read row 0).
   bf16x8_t qb[C::KK];
   {
-    const int qr = row_ok ? gr : tile * 16;
+    const int qr = row_ok ? gr : first_row;
     const int j = qr / p.group, h = kvh * p.group + qr % p.group;
     const uint4* qrow = (const uint4*)((const uint16_t*)p.q + (((int64_t)b * p.q_len + j) * p.num_q_heads + h) * DK);
 #pragma unroll
@@ -135,55 +222,82 @@ __global__ __launch_bounds__(64 * NW) void stage1_mfma_kernel(Stage1Params p) {
   const int64_t vs_page16 = p.vs_page * 2 / 16, vs_tok16 = p.vs_tok * 2 / 16;
 
   // DMA lane mapping: instruction i moves key (i%2)*16 + lane/4, the 4 chunks
-  // (i/2)*4 + ((lane%4) ^ ((key/4)%4)); its LDS slot is i*64 + lane.
+  // (i/2)*4 + ((lane%4) ^ ((key/4)%4)); its LDS slot is i*64 + lane.  With
+  // RW waves on one stream, wave rw issues instructions rw, rw + RW, ...
   const int dkey0 = lane >> 2, dkey1 = 16 + (lane >> 2);
   const int dsw0 = (lane & 3) ^ ((dkey0 >> 2) & 3), dsw1 = (lane & 3) ^ ((dkey1 >> 2) & 3);
-
-  for (int blk = blk0; blk < end_max; blk += NW * 32) {
-    // ---- page walk: offsets of keys blk + (lane & 31) ----
+  auto issue_dma = [&](int blk, int page, int buf) {
     const int t = blk + (lane & 31);
     const int tc = t < end_max ? t : end_max - 1;
-    const int page = page_next;
     const int slot = tc & (P - 1);
     const uint32_t koff = (uint32_t)(page * ks_page16 + slot * ks_tok16);
-    const uint32_t voff = (uint32_t)(page * vs_page16 + slot * vs_tok16);
-    if (blk + NW * 32 < end_max) page_next = page_of(blk + NW * 32);
-
-    // ---- K (and V) rows into the tile ----
-    {
-      const uint32_t k0 = (uint32_t)__shfl((int)koff, dkey0), k1 = (uint32_t)__shfl((int)koff, dkey1);
+    const uint32_t k0 = (uint32_t)__shfl((int)koff, dkey0), k1 = (uint32_t)__shfl((int)koff, dkey1);
+    uint8_t* kt = tile_k(buf);
 #pragma unroll
-      for (int i = 0; i < C::KINS; ++i) {
-        const uint32_t ko = (i & 1) ? k1 : k0;
+    for (int ii = 0; ii < C::KINS / RW; ++ii) {
+      const int i = rw + ii * RW;
+      const uint32_t ko = (i & 1) ? k1 : k0;
+      const int ch = (i >> 1) * 4 + ((i & 1) ? dsw1 : dsw0);
+      lds_dma16(kbase + (uint64_t)ko * 16 + ch * 16, kt + i * 1024);
+    }
+    if constexpr (!VALIAS) {
+      const uint32_t voff = (uint32_t)(page * vs_page16 + slot * vs_tok16);
+      const uint32_t v0 = (uint32_t)__shfl((int)voff, dkey0), v1 = (uint32_t)__shfl((int)voff, dkey1);
+      uint8_t* vt = tile_v(buf);
+#pragma unroll
+      for (int ii = 0; ii < C::VINS / RW; ++ii) {
+        const int i = rw + ii * RW;
+        const uint32_t vo = (i & 1) ? v1 : v0;
         const int ch = (i >> 1) * 4 + ((i & 1) ? dsw1 : dsw0);
-        lds_dma16(kbase + (uint64_t)ko * 16 + ch * 16, ktile + i * 1024);
-      }
-      if constexpr (!VALIAS) {
-        const uint32_t v0 = (uint32_t)__shfl((int)voff, dkey0), v1 = (uint32_t)__shfl((int)voff, dkey1);
-#pragma unroll
-        for (int i = 0; i < C::VINS; ++i) {
-          const uint32_t vo = (i & 1) ? v1 : v0;
-          const int ch = (i >> 1) * 4 + ((i & 1) ? dsw1 : dsw0);
-          lds_dma16(vbase + (uint64_t)vo * 16 + ch * 16, vtile + i * 1024);
-        }
+        lds_dma16(vbase + (uint64_t)vo * 16 + ch * 16, vt + i * 1024);
       }
     }
-    wait_vmcnt<0>();
-    __builtin_amdgcn_wave_barrier();
+  };
 
-    // ---- S^T = K Q^T, two 16-key halves ----
-    f32x4_t st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < C::KK; ++kk) {
-      const int c = kk * 4 + g;
-      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, *(const uint4*)(ktile + tile_slot(n, c) * 16));
-      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, *(const uint4*)(ktile + tile_slot(16 + n, c) * 16));
-      st0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qb[kk], st0, 0, 0, 0);
-      st1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[kk], st1, 0, 0, 0);
-    }
+  // This lane's LDS byte offsets inside a tile.  Q.K step kk reads chunk
+  // kk*4 + g of keys n and 16 + n: slot(k, kk*4 + g) = kk*128 + slot(k, g).
+  // P.V step dt reads chunk 2dt + q4/2 of keys rk0 and rk1 (half q4%2 of
+  // it): slot(k, 2dt + x) = (dt/2)*128 + slot(k, 2(dt%2) + x).  The
+  // column-block step (2048 bytes) goes into the read's immediate offset.
+  const int rk0 = 4 * g + (lane & 15) / 4, rk1 = 16 + rk0;
+  const int q4 = lane & 3, vx = q4 >> 1, half = (q4 & 1) * 8;
+  const uint32_t kq0 = tile_slot(n, g) * 16, kq1 = tile_slot(16 + n, g) * 16;
+  const uint32_t ve0 = tile_slot(rk0, vx) * 16 + half, ve1 = tile_slot(rk1, vx) * 16 + half;
+  const uint32_t vo0 = tile_slot(rk0, 2 + vx) * 16 + half, vo1 = tile_slot(rk1, 2 + vx) * 16 + half;
 
-    // ---- online softmax for query row n over keys 4g+i, 16+4g+i ----
-    float sc[8];
+  // ---- S^T = K Q^T for one tile: two 16-key halves; reads run kLaK steps ahead ----
+  auto qk = [&](const uint8_t* ktile, f32x4_t& st0, f32x4_t& st1) {
+    const uint32_t kt = lds_addr(ktile);
+    st0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    st1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    constexpr int LA = kLaK;
+    i32x4_t kr[LA + 1][2];
+    auto rd = [&](auto ic) {
+      constexpr int kk = decltype(ic)::value;
+      if constexpr (kk < C::KK)
+        lds_read2_b128<kk * 2048>(kr[kk % (LA + 1)][0], kr[kk % (LA + 1)][1], kt + kq0, kt + kq1);
+    };
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (rd(std::integral_constant<int, I>{}), ...);
+    }(std::make_integer_sequence<int, LA>{});
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      auto step = [&](auto ic) {
+        constexpr int kk = decltype(ic)::value;
+        rd(std::integral_constant<int, kk + LA>{});
+        constexpr int ahead = C::KK - 1 - kk < LA ? C::KK - 1 - kk : LA;
+        i32x4_t& r0 = kr[kk % (LA + 1)][0];
+        i32x4_t& r1 = kr[kk % (LA + 1)][1];
+        lds_wait2<2 * ahead>(r0, r1);
+        st0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r0), qb[kk], st0, 0, 0, 0);
+        st1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r1), qb[kk], st1, 0, 0, 0);
+      };
+      (step(std::integral_constant<int, I>{}), ...);
+    }(std::make_integer_sequence<int, C::KK>{});
+  };
+
+  // Scores of query row n for keys 4g+i and 16+4g+i (log2 units, masked),
+  // and their max over the row's 32 keys.
+  auto scores = [&](int blk, const f32x4_t& st0, const f32x4_t& st1, float* sc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k0 = blk + 4 * g + i, k1 = blk + 16 + 4 * g + i;
@@ -194,89 +308,174 @@ __global__ __launch_bounds__(64 * NW) void stage1_mfma_kernel(Stage1Params p) {
 #pragma unroll
     for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[e]);
     bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(m, bm);
-    const float al = mn == kNegInf ? 1.f : fast_exp2(m - mn);
+    return fmaxf(bm, __shfl_xor(bm, 32));
+  };
+
+  // ---- weights against the reference max m, row sum, O^T += V^T P^T ----
+  // Transpose reads run kLaV steps ahead: lane 16g + s addresses 4 dims
+  // (s%4) of key 4g + s/4 (first read) or 16 + 4g + s/4 (second read).
+  auto pv = [&](const uint8_t* vtile, const float* sc) {
+    const uint32_t vt = lds_addr(vtile);
     float pw[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pw[e] = sc[e] == kNegInf ? 0.f : fast_exp2(sc[e] - mn);
-    if (__any(al != 1.f && m != kNegInf)) {
-      l *= al;
-#pragma unroll
-      for (int d = 0; d < C::DT; ++d) acc[d] *= al;
-    }
+    for (int e = 0; e < 8; ++e) pw[e] = sc[e] == kNegInf ? 0.f : fast_exp2(sc[e] - m);
 #pragma unroll
     for (int e = 0; e < 8; ++e) l += pw[e];
-    m = mn;
     uint4 pk;
     pk.x = pack_bf16x2(pw[0], pw[1]);
     pk.y = pack_bf16x2(pw[2], pw[3]);
     pk.z = pack_bf16x2(pw[4], pw[5]);
     pk.w = pack_bf16x2(pw[6], pw[7]);
     const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
+    constexpr int LA = kLaV;
+    i16x4_t vr[LA + 1][2];
+    auto rd = [&](auto ic) {
+      constexpr int dt = decltype(ic)::value;
+      if constexpr (dt < C::DT) {
+        constexpr int off = (dt >> 1) * 2048;
+        if constexpr (dt & 1)
+          lds_read2_tr16<off>(vr[dt % (LA + 1)][0], vr[dt % (LA + 1)][1], vt + vo0, vt + vo1);
+        else
+          lds_read2_tr16<off>(vr[dt % (LA + 1)][0], vr[dt % (LA + 1)][1], vt + ve0, vt + ve1);
+      }
+    };
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (rd(std::integral_constant<int, I>{}), ...);
+    }(std::make_integer_sequence<int, LA>{});
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      auto step = [&](auto ic) {
+        constexpr int dt = decltype(ic)::value;
+        rd(std::integral_constant<int, dt + LA>{});
+        constexpr int ahead = C::DT - 1 - dt < LA ? C::DT - 1 - dt : LA;
+        i16x4_t& r0 = vr[dt % (LA + 1)][0];
+        i16x4_t& r1 = vr[dt % (LA + 1)][1];
+        lds_wait2<2 * ahead>(r0, r1);
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[dt], 0, 0, 0);
+      };
+      (step(std::integral_constant<int, I>{}), ...);
+    }(std::make_integer_sequence<int, C::DT>{});
+  };
 
-    // ---- O^T += V^T P^T ----
-    // Transpose reads: lane 16g + s addresses 4 dims (s%4) of key 4g + s/4
-    // (first read) or 16 + 4g + s/4 (second read).
-    const int rk0 = 4 * g + (lane & 15) / 4, rk1 = 16 + rk0;
-    const int q4 = lane & 3;
+  // Lazy rescale (the online-softmax variant that moves the reference max
+  // only when a block's max exceeds it by more than kLazyLog2): the hot loop
+  // below never touches the accumulators outside the matrix cores, so they
+  // stay in AGPRs; a block that needs a new reference leaves the loop,
+  // rescales here and rejoins.  Weights are then at most 2^kLazyLog2, which
+  // fp32 sums and bf16 weights hold exactly as well as weights <= 1.
+  auto rescale = [&](float bm) {
+    const float mn = fmaxf(m, bm);
+    const float al = mn == kNegInf ? 1.f : fast_exp2(m - mn);
+    if (al != 1.f && m != kNegInf) {
+      l *= al;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const int c = 2 * dt + (q4 >> 1), half = (q4 & 1) * 8;
-      typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-      const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)((__attribute__((address_space(3))) uint8_t*)vtile + tile_slot(rk0, c) * 16 + half));
-      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)((__attribute__((address_space(3))) uint8_t*)vtile + tile_slot(rk1, c) * 16 + half));
-      const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[dt], 0, 0, 0);
+      for (int d = 0; d < C::DT; ++d) acc[d] *= al;
     }
-    __builtin_amdgcn_wave_barrier();
+    m = mn;
+  };
+
+  // Runs blocks [0, nb) of this wave: front(it) makes block it readable and
+  // returns its tile buffer.
+  auto run_blocks = [&](int nb, auto&& front) {
+    float sc[8];
+    float bm = kNegInf;
+    int it = 0;
+    while (it < nb) {
+      int buf = 0;
+      for (; it < nb; ++it) {
+        buf = front(it);
+        f32x4_t st0, st1;
+        qk(tile_k(buf), st0, st1);
+        bm = scores(blk_of(it), st0, st1, sc);
+        if (__any(bm > m + kLazyLog2)) break;
+        pv(tile_v(buf), sc);
+      }
+      if (it < nb) {
+        rescale(bm);
+        pv(tile_v(buf), sc);
+        ++it;
+      }
+    }
+  };
+
+  if constexpr (C::NBUF == 1) {
+    // One wave per key stream, its own tile: load, wait, compute.  Stream
+    // kw has blocks kw, kw + KW, ... below end_max.
+    const int first = sb + kw * 32;
+    const int nb = first < end_max ? (end_max - first + 32 * KW - 1) / (32 * KW) : 0;
+    int page_next = nb > 0 ? page_of(blk_of(0)) : 0;
+    run_blocks(nb, [&](int it) {
+      __builtin_amdgcn_wave_barrier();   // the previous block's reads are done (lds_wait2 to 0)
+      const int page = page_next;
+      if (it + 1 < nb) page_next = page_of(blk_of(it + 1));
+      issue_dma(blk_of(it), page, 0);
+      wait_vmcnt<0>();
+      __builtin_amdgcn_wave_barrier();
+      return 0;
+    });
+  } else if (nit > 0) {    // RW waves share a ring of NBUF tiles; D = NBUF - 1 blocks are in flight
+    // while one is computed.  Iteration it waits for block it, meets the
+    // other waves (block it is then in LDS, and the buffer block it + D
+    // reuses is no longer read), loads the page ids of block it + 2D - 1 and
+    // issues block it + D.  Page ids are thus loaded D - 1 blocks before their
+    // DMA, so the compiler's wait for them never drains the DMA queue, and
+    // the explicit wait for block it counts exactly the loads issued after
+    // it: D - 1 x (one page-id load + this wave's DMAs).  Near the end of the
+    // split fewer blocks follow, and the wait is for everything.
+    constexpr int NB = C::NBUF, D = NB - 1;
+    // Page ids travel through LDS as well: block X's ids are DMA'd into slot
+    // X % NB of this wave's ring (lane k: key k % 32) just before block X - D
+    // is issued, so the wait for block X - D covers them.  A page id loaded
+    // into a register would make the compiler wait for every DMA in flight
+    // before its first use.
+    uint8_t* pid_ring = smem + C::TILES + wave * NB * 256;
+    const uint32_t pid_addr = lds_addr(pid_ring) + lane * 4;
+    auto issue_pid = [&](int blk_idx, int slot) {
+      const int t = blk_of(blk_idx) + (lane & 31);
+      const int tc = t < end_max ? t : end_max - 1;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(pt + (tc >> psh)),
+                                       (__attribute__((address_space(3))) void*)(pid_ring + slot * 256), 4, 0, 0);
+    };
+    auto read_pid = [&](int slot) {
+      int v = lds_read_b32<0>(pid_addr + slot * 256);
+      lds_wait1<0>(v);
+      return v;
+    };
+    // Prologue: ids of blocks 0 .. D-1, then blocks 0 .. D-1 themselves
+    // (each preceded by the ids of block j + D).
+#pragma unroll
+    for (int j = 0; j < D; ++j) issue_pid(j, j);
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      issue_pid(j + D, (j + D) % NB);
+      const int pg = read_pid(j);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j < nit) issue_dma(blk_of(j), pg, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Iteration it: wait for block it (all but the D - 1 later steps of
+    // this wave: page ids + DMAs), meet, queue the ids of block it + 2D and
+    // block it + D, then compute block it.
+    run_blocks(nit, [&](int it) {
+      if (it + D <= nit) {
+        wait_vmcnt<(D - 1) * (C::MINE + 1)>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      tile_barrier();
+      issue_pid(it + 2 * D, (it + 2 * D) % NB);
+      const int pg = read_pid((it + D) % NB);
+      __builtin_amdgcn_sched_barrier(0);
+      if (it + D < nit) issue_dma(blk_of(it + D), pg, (it + D) % NB);
+      __builtin_amdgcn_sched_barrier(0);
+      return it % NB;
+    });
   }
 
-  // ---- wave state into LDS: acc^T [16 rows][DV], m[16], l[16] ----
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  float* pacc = (float*)(smem + wave * C::WAVE_B);
-  float* pml = pacc + 16 * DV;
-  // Lane l holds O^T[dims dt*16 + 4g + i][row n].
-#pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt)
-    *(float4*)(pacc + n * DV + dt * 16 + 4 * g) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-  if (g == 0) {
-    pml[n] = m;
-    pml[16 + n] = l;
-  }
-  __syncthreads();
-
-  // ---- merge the NW waves: thread -> (row, 4 dims) ----
-  for (int idx = threadIdx.x; idx < 16 * DV / 4; idx += 64 * NW) {
-    const int r = idx / (DV / 4), d = (idx % (DV / 4)) * 4;
-    const int grr = tile * 16 + r;
-    if (grr >= p.rows_total) continue;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, ((const float*)(smem + w * C::WAVE_B))[16 * DV + r]);
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    float lse = kNegInf;
-    if (M != kNegInf) {
-      float den = 0.f;
-      float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float* base = (const float*)(smem + w * C::WAVE_B);
-        const float f = fast_exp2(base[16 * DV + r] - M);
-        den += f * base[16 * DV + 16 + r];
-        const float4 a = *(const float4*)(base + r * DV + d);
-        num.x += f * a.x;
-        num.y += f * a.y;
-        num.z += f * a.z;
-        num.w += f * a.w;
-      }
-      const float inv = 1.f / den;
-      o = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
-      lse = (M + __log2f(den)) * kLn2;
-    }
+  auto write_row = [&](int grr, int d, float4 o, float lse) {
     const int j = grr / p.group, h = kvh * p.group + grr % p.group;
     const int64_t row = ((int64_t)b * p.q_len + j) * p.num_q_heads + h;
     if (p.out) {
@@ -286,37 +485,109 @@ __global__ __launch_bounds__(64 * NW) void stage1_mfma_kernel(Stage1Params p) {
       *(float4*)(p.o_part + (row * p.num_splits + s) * DV + d) = o;
       if (d == 0) p.lse_part[row * p.num_splits + s] = lse;
     }
+  };
+
+  if constexpr (KW == 1) {
+    // The wave holds its rows' complete state: normalise and write.
+    if (row_ok) {
+      const bool empty = m == kNegInf;
+      const float inv = empty ? 0.f : 1.f / l;
+      const float lse = empty ? kNegInf : (m + __log2f(l)) * kLn2;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+        write_row(gr, dt * 16 + 4 * g,
+                  make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv), lse);
+    }
+  } else {
+    // ---- wave state into LDS: acc^T [16 rows][DV], m[16], l[16] ----
+    __syncthreads();  // the tiles are no longer read
+    float* pacc = (float*)(smem + wave * C::PART);
+    float* pml = pacc + 16 * DV;
+    // Lane l holds O^T[dims dt*16 + 4g + i][row n].
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+      *(float4*)(pacc + n * DV + dt * 16 + 4 * g) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    if (g == 0) {
+      pml[n] = m;
+      pml[16 + n] = l;
+    }
+    __syncthreads();
+
+    // ---- merge the KW streams of each row tile: thread -> (row, 4 dims) ----
+    for (int idx = threadIdx.x; idx < RW * 16 * DV / 4; idx += 64 * C::NW) {
+      const int rt = idx / (16 * DV / 4);
+      const int r = (idx / (DV / 4)) % 16, d = (idx % (DV / 4)) * 4;
+      const int grr = (tile * RW + rt) * 16 + r;
+      if (grr >= p.rows_total) continue;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < KW; ++w)
+        M = fmaxf(M, ((const float*)(smem + (w * RW + rt) * C::PART))[16 * DV + r]);
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      float lse = kNegInf;
+      if (M != kNegInf) {
+        float den = 0.f;
+        float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int w = 0; w < KW; ++w) {
+          const float* base = (const float*)(smem + (w * RW + rt) * C::PART);
+          const float f = fast_exp2(base[16 * DV + r] - M);
+          den += f * base[16 * DV + 16 + r];
+          const float4 a = *(const float4*)(base + r * DV + d);
+          num.x += f * a.x;
+          num.y += f * a.y;
+          num.z += f * a.z;
+          num.w += f * a.w;
+        }
+        const float inv = 1.f / den;
+        o = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+        lse = (M + __log2f(den)) * kLn2;
+      }
+      write_row(grr, d, o, lse);
+    }
   }
 }
 
 struct Entry {
   int dk, dv;
   bool valias;
+  int rw, kw;
   void (*fn)(Stage1Params);
 };
 
 constexpr Entry kTable[] = {
-    {576, 512, true, &stage1_mfma_kernel<576, 512, true, 4>},
-    {256, 256, false, &stage1_mfma_kernel<256, 256, false, 4>},
-    {128, 128, false, &stage1_mfma_kernel<128, 128, false, 4>},
+    {576, 512, true, 1, 4, &stage1_mfma_kernel<576, 512, true, 1, 4>},
+    {576, 512, true, 4, 1, &stage1_mfma_kernel<576, 512, true, 4, 1>},
+    {256, 256, false, 1, 4, &stage1_mfma_kernel<256, 256, false, 1, 4>},
+    {128, 128, false, 1, 4, &stage1_mfma_kernel<128, 128, false, 1, 4>},
 };
 
-const Entry* find(int dk, int dv, bool valias) {
+const Entry* find(int dk, int dv, bool valias, int rw) {
   for (const Entry& e : kTable)
-    if (e.dk == dk && e.dv == dv && e.valias == valias) return &e;
+    if (e.dk == dk && e.dv == dv && e.valias == valias && e.rw == rw) return &e;
   return nullptr;
 }
 
 }  // namespace
 
 bool stage1_mfma_supported(int dtype, int dk, int dv, bool v_aliases_k) {
-  return dtype == 1 && find(dk, dv, v_aliases_k) != nullptr;
+  return dtype == 1 && find(dk, dv, v_aliases_k, 1) != nullptr;
 }
 
-hipError_t launch_stage1_mfma(const Stage1Params& p, int dk, int dv, bool v_aliases_k, hipStream_t st) {
-  const Entry* e = find(dk, dv, v_aliases_k);
+int stage1_mfma_row_tiles(int dk, int dv, bool v_aliases_k, int rows) {
+  // Several 16-row tiles share one K stream only when there are enough rows
+  // to fill all of them (the wide MLA shape); otherwise one tile per wave.
+  for (int rw : {4}) {
+    if (rows >= 16 * rw && find(dk, dv, v_aliases_k, rw)) return rw;
+  }
+  return 1;
+}
+
+hipError_t launch_stage1_mfma(const Stage1Params& p, int dk, int dv, bool v_aliases_k, int row_tiles,
+                              hipStream_t st) {
+  const Entry* e = find(dk, dv, v_aliases_k, row_tiles);
   if (!e) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(e->fn, dim3(p.num_wgs), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(e->fn, dim3(p.num_wgs), dim3(64 * e->rw * e->kw), 0, st, p);
   return hipGetLastError();
 }
 

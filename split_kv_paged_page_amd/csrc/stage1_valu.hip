@@ -391,14 +391,14 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
 }
 
 struct Entry {
-  int dtype, dk, dv, rt;
+  int dtype, dk, dv, rt, nw;
   void (*fn[2])(Stage1Params);  // [q rows contiguous]
 };
 
-template <int DTYPE, int DK, int DV, int RT>
+template <int DTYPE, int DK, int DV, int RT, int NW = 4>
 constexpr Entry entry() {
-  return {DTYPE, DK, DV, RT, {&stage1_valu_kernel<DTYPE, DK, DV, RT, 4, false>,
-                              &stage1_valu_kernel<DTYPE, DK, DV, RT, 4, true>}};
+  return {DTYPE, DK, DV, RT, NW, {&stage1_valu_kernel<DTYPE, DK, DV, RT, NW, false>,
+                                  &stage1_valu_kernel<DTYPE, DK, DV, RT, NW, true>}};
 }
 
 constexpr Entry kTable[] = {
@@ -423,7 +423,7 @@ bool stage1_valu_supported(int dtype, int dk, int dv, int rows_per_wg) {
 hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, bool q_contig, hipStream_t st) {
   const Entry* e = find(dtype, dk, dv, p.rows_per_wg);
   if (!e) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(e->fn[q_contig ? 1 : 0], dim3(p.num_wgs), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(e->fn[q_contig ? 1 : 0], dim3(p.num_wgs), dim3(64 * e->nw), 0, st, p);
   return hipGetLastError();
 }
 
