@@ -27,11 +27,16 @@
 //     instruction (each 16-lane group transposes a 4-key x 16-dim block).
 //     The MFMA's key slots follow the score layout, so no shuffle is needed.
 // Tile layout (16-byte units, 32 keys): chunk c of key k sits at
-//   (c/4)*128 + k*4 + ((c%4) ^ ((k/4)%4)).
-// The XOR keeps both read patterns at the LDS bank floor: the 16-byte Q.K
-// reads hit each bank 4 times per wave, the 8-byte transpose reads twice
-// (rocm-libraries PR #10102, Motivation bank table: 4 lanes per bank is the
-// ds_read_b128 floor on gfx950).
+//   (c/4)*128 + k*4 + ((c%4) ^ swz(k)),  swz(k) = (-(k/4)) mod 4.
+// gfx950 LDS has 64 four-byte banks (rocm-libraries PR #10102, Motivation
+// bank table) and serves 256 bytes per cycle, so a read is split into
+// phases that must each touch every bank once.  Measured on MI355X: a
+// 16-byte read's phase is lane quads {0, 3} of one 16-lane window w plus
+// quads {1, 2} of window w ^ 1; an 8-byte read's phases are lanes 0-31 and
+// 32-63.  With swz, the Q.K reads (window g = chunk column, lane n%16 = key)
+// and the transpose reads (groups g, g + 1 on one chunk pair) both sweep all
+// 64 banks in every phase.  The plain (k/4)%4, or its two bits swapped,
+// leaves one of the two patterns two lanes deep per bank.
 #include <utility>
 
 #include "device_common.h"
@@ -74,7 +79,8 @@ struct MCfg {
 };
 
 // 16-byte slot of chunk c of key k (k < 32) in a tile.
-__device__ __forceinline__ int tile_slot(int k, int c) { return (c >> 2) * 128 + k * 4 + ((c & 3) ^ ((k >> 2) & 3)); }
+__device__ __forceinline__ int tile_swz(int k) { return (-(k >> 2)) & 3; }
+__device__ __forceinline__ int tile_slot(int k, int c) { return (c >> 2) * 128 + k * 4 + ((c & 3) ^ tile_swz(k)); }
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
@@ -222,10 +228,10 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   const int64_t vs_page16 = p.vs_page * 2 / 16, vs_tok16 = p.vs_tok * 2 / 16;
 
   // DMA lane mapping: instruction i moves key (i%2)*16 + lane/4, the 4 chunks
-  // (i/2)*4 + ((lane%4) ^ ((key/4)%4)); its LDS slot is i*64 + lane.  With
+  // (i/2)*4 + ((lane%4) ^ swz(key)); its LDS slot is i*64 + lane.  With
   // RW waves on one stream, wave rw issues instructions rw, rw + RW, ...
   const int dkey0 = lane >> 2, dkey1 = 16 + (lane >> 2);
-  const int dsw0 = (lane & 3) ^ ((dkey0 >> 2) & 3), dsw1 = (lane & 3) ^ ((dkey1 >> 2) & 3);
+  const int dsw0 = (lane & 3) ^ tile_swz(dkey0), dsw1 = (lane & 3) ^ tile_swz(dkey1);
   auto issue_dma = [&](int blk, int page, int buf) {
     const int t = blk + (lane & 31);
     const int tc = t < end_max ? t : end_max - 1;

@@ -14,7 +14,7 @@ import pytest
 import oracle
 from tests.gpu_helpers import Decode, lse_err, row_rel_err, say, tol_for
 from workloads import generate, get, scaled
-from workloads.gen import designate
+from workloads.gen import designate, ramp
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +83,20 @@ def test_parity_small(name):
     e_out, e_lse = check_against_oracle(d, tol_for(w))
     print(f"{name}: S={d.S} rows/wg={d.plan.rows_per_wg} tiles={d.plan.head_tiles} "
           f"out {e_out:.2e} lse {e_lse:.2e}")
+
+
+@pytest.mark.parametrize("name", ["gqa_64k_s5000", "mla_b4_private", "mla_wide_b4", "varlen_drafts"])
+@pytest.mark.parametrize("top,q_gain", [(4.0, 1.0), (1.0, 8.0), (3.0, 4.0)])
+def test_parity_rising_and_peaked_scores(name, top, q_gain):
+    # Keys scaled up along the context (and/or a peaked q) make the running
+    # max climb through many blocks, in steps both below and above the lazy
+    # rescale slack, so both the hot loop and its rescale exit are checked.
+    w = dict(small_cases(), mla_b4_private=scaled("mla_b48", context_lens=(3000, 1, 2100, 4097), prefix_len=0,
+                                                  prefix_group=0))[name]
+    inp = ramp(inputs(name, w), top, q_gain)
+    say(f"rising {name} top={top} q_gain={q_gain}")
+    d = Decode(inp, num_splits=w.num_splits).run()
+    check_against_oracle(d, tol_for(w))
 
 
 @pytest.mark.parametrize("name,splits", [("gqa_tiny_f32", (1, 2, 4, 7, 16)),

@@ -136,3 +136,27 @@ def designate(inp: Inputs, tokens) -> Inputs:
     q[...] = _encode(np.zeros(1, np.float32), w.kv_dtype)[0]
     q[..., lo:] = _encode(np.ones(1, np.float32), w.kv_dtype)[0]
     return inp.with_(q=q, k_cache=k, scale=np.float32(1.0))
+
+
+def ramp(inp: Inputs, top: float, q_gain: float = 1.0) -> Inputs:
+    """Scores that rise along the context: the K row of request b's key t is
+    multiplied by 1 + (top - 1) * t / (L_b - 1), and q by ``q_gain``.  The
+    running max of a split then moves up many times, by small and large steps.
+    When V aliases K the V rows scale with their keys.  Requests must not share
+    pages (no prefix groups): a shared row would take the last request's factor.
+    """
+    w = inp.w
+    if w.prefix_group:
+        raise ValueError("ramp needs private pages")
+    P = w.page_size
+    as_f32 = (lambda a: a) if w.kv_dtype == "f32" else \
+        (lambda a: (a.astype(np.uint32) << np.uint32(16)).view(np.float32))
+    k = inp.k_cache.copy()
+    for b in range(w.batch):
+        L = int(inp.context_lens[b])
+        for t in range(L):
+            f = np.float32(1.0 + (top - 1.0) * t / max(L - 1, 1))
+            page = inp.page_table[b, t // P]
+            k[page, :, t % P, :] = _encode(as_f32(k[page, :, t % P, :]) * f, w.kv_dtype)
+    q = _encode(as_f32(inp.q) * np.float32(q_gain), w.kv_dtype) if q_gain != 1.0 else inp.q
+    return inp.with_(q=q, k_cache=k)
