@@ -64,6 +64,41 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Max / sum of x over lanes l and l ^ 16 (l ^ 32) with the gfx950 lane
+// swaps, no LDS round trip.  v_permlane16_swap a, b (a = b = x on entry)
+// leaves a = x[l], b = x[l+16] on even 16-lane rows and a = x[l-16], b = x[l]
+// on odd rows; v_permlane32_swap does the same across the two 32-lane
+// halves.  Both lanes of a pair see both values (max and a two-term sum are
+// symmetric, so the pair gets the same bits).  Written as assembly: the
+// compiler's builtin folds max(a, b) / a + b of the pair as if a == b.  The
+// s_nop covers the wait states a VALU write needs before a permlane reads it.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  float a = x, b = x;
+  swap16(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float a = x, b = x;
+  swap32(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  float a = x, b = x;
+  swap16(a, b);
+  return a + b;
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float a = x, b = x;
+  swap32(a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 

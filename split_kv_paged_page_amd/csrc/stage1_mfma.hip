@@ -134,12 +134,6 @@ __device__ __forceinline__ int lds_read_b32(uint32_t a) {
 }
 
 template <int N, typename T>
-__device__ __forceinline__ void lds_wait1(T& r0) {
-  static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r0) : "i"(N));
-}
-
-template <int N, typename T>
 __device__ __forceinline__ void lds_wait2(T& r0, T& r1) {
   static_assert(N >= 0 && N < 16, "lgkmcnt range");
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r0), "+v"(r1) : "i"(N));
@@ -200,11 +194,6 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   // streams run the same trip count so shared-tile barriers stay uniform.
   const int nit = (end_max - sb + 32 * KW - 1) / (32 * KW);
   auto blk_of = [&](int it) { return sb + (kw + it * KW) * 32; };
-  auto page_of = [&](int blk) {
-    const int t = blk + (lane & 31);
-    const int tc = t < end_max ? t : end_max - 1;
-    return pt[tc >> psh];
-  };
 
   // Query rows as the B operand of S^T = K Q^T: lane l holds
   // q[row n][kk*32 + g*8 .. +7] for every kk (rows past the group read row 0).
@@ -232,12 +221,14 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   // RW waves on one stream, wave rw issues instructions rw, rw + RW, ...
   const int dkey0 = lane >> 2, dkey1 = 16 + (lane >> 2);
   const int dsw0 = (lane & 3) ^ tile_swz(dkey0), dsw1 = (lane & 3) ^ tile_swz(dkey1);
-  auto issue_dma = [&](int blk, int page, int buf) {
-    const int t = blk + (lane & 31);
-    const int tc = t < end_max ? t : end_max - 1;
-    const int slot = tc & (P - 1);
-    const uint32_t koff = (uint32_t)(page * ks_page16 + slot * ks_tok16);
-    const uint32_t k0 = (uint32_t)__shfl((int)koff, dkey0), k1 = (uint32_t)__shfl((int)koff, dkey1);
+  // page0 / page1: page ids of keys blk + dkey0 and blk + dkey1 (clamped to
+  // the last visible key like every other key).
+  auto issue_dma = [&](int blk, int page0, int page1, int buf) {
+    const int t0 = blk + dkey0, t1 = blk + dkey1;
+    const int s0 = (t0 < end_max ? t0 : end_max - 1) & (P - 1);
+    const int s1 = (t1 < end_max ? t1 : end_max - 1) & (P - 1);
+    const uint32_t k0 = (uint32_t)(page0 * ks_page16 + s0 * ks_tok16);
+    const uint32_t k1 = (uint32_t)(page1 * ks_page16 + s1 * ks_tok16);
     uint8_t* kt = tile_k(buf);
 #pragma unroll
     for (int ii = 0; ii < C::KINS / RW; ++ii) {
@@ -247,8 +238,8 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
       lds_dma16(kbase + (uint64_t)ko * 16 + ch * 16, kt + i * 1024);
     }
     if constexpr (!VALIAS) {
-      const uint32_t voff = (uint32_t)(page * vs_page16 + slot * vs_tok16);
-      const uint32_t v0 = (uint32_t)__shfl((int)voff, dkey0), v1 = (uint32_t)__shfl((int)voff, dkey1);
+      const uint32_t v0 = (uint32_t)(page0 * vs_page16 + s0 * vs_tok16);
+      const uint32_t v1 = (uint32_t)(page1 * vs_page16 + s1 * vs_tok16);
       uint8_t* vt = tile_v(buf);
 #pragma unroll
       for (int ii = 0; ii < C::VINS / RW; ++ii) {
@@ -313,8 +304,7 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
     float bm = sc[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[e]);
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    return fmaxf(bm, __shfl_xor(bm, 32));
+    return max_xor32(max_xor16(bm));
   };
 
   // ---- weights against the reference max m, row sum, O^T += V^T P^T ----
@@ -409,12 +399,19 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
     // kw has blocks kw, kw + KW, ... below end_max.
     const int first = sb + kw * 32;
     const int nb = first < end_max ? (end_max - first + 32 * KW - 1) / (32 * KW) : 0;
-    int page_next = nb > 0 ? page_of(blk_of(0)) : 0;
+    // Page ids of this lane's two DMA keys, one block ahead.
+    auto pages_of = [&](int blk, int& p0, int& p1) {
+      const int t0 = blk + dkey0, t1 = blk + dkey1;
+      p0 = pt[(t0 < end_max ? t0 : end_max - 1) >> psh];
+      p1 = pt[(t1 < end_max ? t1 : end_max - 1) >> psh];
+    };
+    int pn0 = 0, pn1 = 0;
+    if (nb > 0) pages_of(blk_of(0), pn0, pn1);
     run_blocks(nb, [&](int it) {
       __builtin_amdgcn_wave_barrier();   // the previous block's reads are done (lds_wait2 to 0)
-      const int page = page_next;
-      if (it + 1 < nb) page_next = page_of(blk_of(it + 1));
-      issue_dma(blk_of(it), page, 0);
+      const int p0 = pn0, p1 = pn1;
+      if (it + 1 < nb) pages_of(blk_of(it + 1), pn0, pn1);
+      issue_dma(blk_of(it), p0, p1, 0);
       wait_vmcnt<0>();
       __builtin_amdgcn_wave_barrier();
       return 0;
@@ -435,17 +432,18 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
     // into a register would make the compiler wait for every DMA in flight
     // before its first use.
     uint8_t* pid_ring = smem + C::TILES + wave * NB * 256;
-    const uint32_t pid_addr = lds_addr(pid_ring) + lane * 4;
+    const uint32_t pid_addr = lds_addr(pid_ring) + dkey0 * 4;   // entry k: key k % 32
     auto issue_pid = [&](int blk_idx, int slot) {
       const int t = blk_of(blk_idx) + (lane & 31);
       const int tc = t < end_max ? t : end_max - 1;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(pt + (tc >> psh)),
                                        (__attribute__((address_space(3))) void*)(pid_ring + slot * 256), 4, 0, 0);
     };
-    auto read_pid = [&](int slot) {
-      int v = lds_read_b32<0>(pid_addr + slot * 256);
-      lds_wait1<0>(v);
-      return v;
+    // This lane's two DMA keys' page ids from ring slot `slot` (the caller
+    // waits for them with lds_wait2).
+    auto read_pids = [&](int slot, int& p0, int& p1) {
+      p0 = lds_read_b32<0>(pid_addr + slot * 256);
+      p1 = lds_read_b32<64>(pid_addr + slot * 256);
     };
     // Prologue: ids of blocks 0 .. D-1, then blocks 0 .. D-1 themselves
     // (each preceded by the ids of block j + D).
@@ -455,32 +453,36 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       issue_pid(j + D, (j + D) % NB);
-      const int pg = read_pid(j);
+      int p0, p1;
+      read_pids(j, p0, p1);
+      lds_wait2<0>(p0, p1);
       __builtin_amdgcn_sched_barrier(0);
-      if (j < nit) issue_dma(blk_of(j), pg, j);
+      if (j < nit) issue_dma(blk_of(j), p0, p1, j);
       __builtin_amdgcn_sched_barrier(0);
     }
     // Iteration it: wait for block it (all but the D - 1 later steps of
-    // this wave: page ids + DMAs), meet, queue the ids of block it + 2D and
-    // block it + D, then compute block it.
+    // this wave: page ids + DMAs), read the ids of block it + D (they came
+    // with block it), meet, queue the ids of block it + 2D and block it + D,
+    // then compute block it.
     run_blocks(nit, [&](int it) {
       if (it + D <= nit) {
         wait_vmcnt<(D - 1) * (C::MINE + 1)>();
       } else {
         wait_vmcnt<0>();
       }
+      int p0, p1;
+      read_pids((it + D) % NB, p0, p1);
       tile_barrier();
       issue_pid(it + 2 * D, (it + 2 * D) % NB);
-      const int pg = read_pid((it + D) % NB);
+      lds_wait2<0>(p0, p1);
       __builtin_amdgcn_sched_barrier(0);
-      if (it + D < nit) issue_dma(blk_of(it + D), pg, (it + D) % NB);
+      if (it + D < nit) issue_dma(blk_of(it + D), p0, p1, (it + D) % NB);
       __builtin_amdgcn_sched_barrier(0);
       return it % NB;
     });
   }
 
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = sum_xor32(sum_xor16(l));
   auto write_row = [&](int grr, int d, float4 o, float lse) {
     const int j = grr / p.group, h = kvh * p.group + grr % p.group;
     const int64_t row = ((int64_t)b * p.q_len + j) * p.num_q_heads + h;
