@@ -84,8 +84,8 @@ __device__ __forceinline__ int tile_slot(int k, int c) { return (c >> 2) * 128 +
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kLaK = 2;  // Q.K read steps in flight ahead of the MFMA
-constexpr int kLaV = 3;  // P.V read steps in flight ahead of the MFMA
+constexpr int kLaK = 4;  // Q.K read steps in flight ahead of the MFMA
+constexpr int kLaV = 6;  // P.V read steps in flight ahead of the MFMA
 constexpr float kLazyLog2 = 8.f;  // reference-max slack (log2 units) before a rescale
 
 __device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
