@@ -116,7 +116,8 @@ typedef struct attn_decode_plan_t {
   int32_t variant;            /* ATTN_VARIANT_* */
   int32_t rows_per_wg;        /* query rows one stage-1 workgroup scores */
   int32_t head_tiles;         /* stage-1 workgroups per (request, KV head, split) */
-  int32_t stage2_tiles;       /* Dv slices per query row in stage 2 at num_splits */
+  int32_t stage2_tiles;       /* Dv slices per query row of the stage-2 merge when it runs
+                                 more than 16 splits (16 or fewer: one thread per 4 dims) */
   int32_t xcd_remap;          /* 1: split-major, XCD-contiguous workgroup order */
   int32_t flags;              /* ATTN_PLAN_* given to attn_decode_plan */
   int64_t workspace_bytes;    /* bytes the caller must provide at max_splits */

@@ -2,16 +2,21 @@
 // partials (aiter PR #4758, "[Gluon][MLA] Deeper async-copy pipeline in the
 // bh16 stage-1 decode loop", Technical Details item 3).
 //
-// One workgroup per (query row, Dv slice).  With few query rows (batch-1
-// decode) the host cuts the head dim into up to 8 slices so more CUs work;
-// each slice re-derives the row's max and weight sum on its own, so slices
-// never talk to each other.  256 threads = SL split lanes x (256 / SL)
-// four-float columns, SL = the largest power of two <= min(S, 16); split
-// lane sl sums splits sl, sl + SL, ... and the lanes are then added in lane
-// order.  Every summation order depends on the split count only, never on
-// the slicing, so sliced and unsliced merges give the same bits.  The
-// partial-output loads are issued before the weights are known, so the
-// merge costs one memory round trip.
+// Two kernels, chosen by the split count alone, so a given S always merges
+// in the same order (same bits for every tiling and launch shape):
+//
+// * S <= kRowSplits (many rows, few splits: MLA batches, wide GQA): one
+//   thread per (query row, 4 dims) walks the splits in order; no LDS, no
+//   barrier, every load issued up front.
+// * larger S (batch-1 decode): one workgroup per (query row, Dv slice).  With
+//   few query rows the host cuts the head dim into up to 8 slices so more
+//   CUs work; each slice re-derives the row's max and weight sum on its own,
+//   so slices never talk to each other.  256 threads = SL split lanes x
+//   (256 / SL) four-float columns, SL = the largest power of two <= min(S,
+//   16); split lane sl sums splits sl, sl + SL, ... and the lanes are then
+//   added in lane order.  Every summation order depends on the split count
+//   only, never on the slicing.  The partial-output loads are issued before
+//   the weights are known, so the merge costs one memory round trip.
 #include "device_common.h"
 #include "launch.h"
 
@@ -125,6 +130,54 @@ __global__ __launch_bounds__(kThreads) void stage2_kernel(Stage2Params p) {
   if (p.lse && tile == 0 && tid == 0) p.lse[row] = M == kNegInf ? kNegInf : M + __logf(den);
 }
 
+constexpr int kRowSplits = 16;
+
+template <int DTYPE>
+__global__ __launch_bounds__(kThreads) void stage2_rows_kernel(Stage2Params p) {
+  const int Dv = p.head_dim_v;
+  const int cols = Dv / 4;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t row = idx / cols;
+  if (row >= p.rows) return;
+  const int c = (int)(idx % cols);
+  const int S = p.num_splits;
+  const float* lse_row = p.lse_part + row * S;
+  const float* base = p.o_part + row * S * Dv + c * 4;
+  float4 ov[kRowSplits];
+  float ls[kRowSplits];
+#pragma unroll
+  for (int s = 0; s < kRowSplits; ++s) {
+    if (s < S) {
+      ov[s] = *(const float4*)(base + (int64_t)s * Dv);
+      ls[s] = lse_row[s];
+    }
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int s = 0; s < kRowSplits; ++s)
+    if (s < S) M = fmaxf(M, ls[s]);
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  if (M != kNegInf) {
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int s = 0; s < kRowSplits; ++s) {
+      if (s < S) {
+        const float wgt = fast_exp2((ls[s] - M) * kLog2e);
+        den += wgt;
+        t.x = fmaf(wgt, ov[s].x, t.x);
+        t.y = fmaf(wgt, ov[s].y, t.y);
+        t.z = fmaf(wgt, ov[s].z, t.z);
+        t.w = fmaf(wgt, ov[s].w, t.w);
+      }
+    }
+    const float inv = 1.f / den;
+    o = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+  }
+  store_out4(p.out, DTYPE, row * Dv + c * 4, o);
+  if (p.lse && c == 0) p.lse[row] = M == kNegInf ? kNegInf : M + __logf(den);
+}
+
 }  // namespace
 
 bool stage2_supported(int dtype, int dv, int tiles) {
@@ -136,6 +189,15 @@ bool stage2_supported(int dtype, int dv, int tiles) {
 
 hipError_t launch_stage2(const Stage2Params& p, int dtype, hipStream_t st) {
   if (p.num_splits > kMaxSplitsLds) return hipErrorInvalidValue;
+  if (p.num_splits <= kRowSplits) {
+    const int64_t threads = (int64_t)p.rows * (p.head_dim_v / 4);
+    const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
+    if (dtype == 0)
+      hipLaunchKernelGGL(stage2_rows_kernel<0>, grid, dim3(kThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL(stage2_rows_kernel<1>, grid, dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+  }
   const dim3 grid(p.rows * p.tiles);
   if (dtype == 0)
     hipLaunchKernelGGL(stage2_kernel<0>, grid, dim3(kThreads), 0, st, p);
