@@ -354,7 +354,9 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   };
 
   // Lazy rescale (the online-softmax variant that moves the reference max
-  // only when a block's max exceeds it by more than kLazyLog2): the hot loop
+  // only when a block's max exceeds it by more than kLazyLog2; rocm-libraries
+  // PR #10102, Risk Assessment, lists such a switch for its attention
+  // kernel): the hot loop
   // below never touches the accumulators outside the matrix cores, so they
   // stay in AGPRs; a block that needs a new reference leaves the loop,
   // rescales here and rejoins.  Weights are then at most 2^kLazyLog2, which
