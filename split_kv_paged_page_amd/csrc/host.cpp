@@ -172,13 +172,10 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   p.vs_page = d.v_stride_page;
   p.vs_head = d.v_stride_head;
   p.vs_tok = d.v_stride_tok;
-  // Query rows of one workgroup are contiguous in q when they all belong to
-  // one query position: every tile then lies inside one GQA group.
-  const bool q_contig = (p.group % plan->rows_per_wg) == 0 || (d.q_len == 1 && p.rows_total == plan->rows_per_wg);
   hipError_t e = plan->variant == ATTN_VARIANT_MFMA
                      ? splitkv::launch_stage1_mfma(p, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0,
                                                    plan->rows_per_wg / 16, st)
-                     : splitkv::launch_stage1_valu(p, d.dtype, d.head_dim_qk, d.head_dim_v, q_contig, st);
+                     : splitkv::launch_stage1_valu(p, d.dtype, d.head_dim_qk, d.head_dim_v, st);
   if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
   return ATTN_OK;
 }

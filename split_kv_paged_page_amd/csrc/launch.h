@@ -44,7 +44,7 @@ struct Stage2Params {
 
 // Stage-1 launchers; return false when no kernel exists for the shape.
 bool stage1_valu_supported(int dtype, int dk, int dv, int rows_per_wg);
-hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, bool q_contig, hipStream_t s);
+hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, hipStream_t s);
 
 bool stage1_mfma_supported(int dtype, int dk, int dv, bool v_aliases_k);
 int stage1_mfma_row_tiles(int dk, int dv, bool v_aliases_k, int rows);

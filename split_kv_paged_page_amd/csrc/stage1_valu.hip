@@ -56,12 +56,13 @@ struct Cfg {
   static constexpr int KTILE = KLDS ? KINS * GP : 0;
   static constexpr int PART = 4 * RT * DV * 4 + 4 * RT * 2 * 4;  // 4 DPP rows: acc, then m, l
   static constexpr int WAVE_B = ((KTILE > PART ? KTILE : PART) + 15) / 16 * 16;
-  static constexpr int SMEM = NW * WAVE_B;
+  static constexpr int QB = RT * KRB;            // the workgroup's query rows
+  static constexpr int SMEM = NW * WAVE_B + QB;
   static_assert(VRB % 256 == 0 && KRB % 16 == 0, "row sizes");
   static_assert(RT * VE <= 128, "accumulator budget");
 };
 
-template <int DTYPE, int DK, int DV, int RT, int NW, bool QC>
+template <int DTYPE, int DK, int DV, int RT, int NW>
 __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
   using C = Cfg<DTYPE, DK, DV, RT, NW>;
   constexpr int ES = C::ES, KRB = C::KRB, KCH = C::KCH, VU4 = C::VU4, VE = C::VE;
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
   const int g = lane >> 4;
   const int x = lane & 15;
-  uint8_t* wave_lds = smem + wave * C::WAVE_B;
+  uint8_t* wave_lds = smem + C::QB + wave * C::WAVE_B;
 
   int lid = logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap);
   const int tile = lid % p.head_tiles;
@@ -116,30 +117,24 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
   int blk0 = sb + wave * 64;
   int page_next = blk0 < end_max ? page_of(blk0) : 0;
 
-  // Query rows are wave-uniform: read through the constant address space
-  // they become scalar loads into SGPRs, and v_dot2 takes them as its scalar
-  // operand, so the broadcast costs neither LDS bandwidth nor VGPRs.  Rows
-  // past the group point at row 0 of the tile (their scores are masked).
-  const qconst_t* qrow[RT];
-  if constexpr (QC) {
-    // The tile's rows are consecutive query heads of one query position:
-    // one base and constant offsets (immediate offsets of s_load).
-    const int gr = tile * RT;
+  // The workgroup's query rows are read by every lane (lane = key): staged
+  // once in LDS, each chunk of each row is one broadcast ds_read_b128 (all
+  // lanes, one address).  Scalar loads would serve the broadcast for free,
+  // but scalar loads return out of order, so every use waits for all of
+  // them: one scalar-memory round trip per chunk.  LDS reads return in
+  // order and pipeline.  Rows past the group repeat row 0 of the tile (their
+  // scores are masked).
+  uint8_t* q_lds = smem;   // first, so row/chunk offsets fit a ds_read immediate
+  for (int idx = threadIdx.x; idx < RT * KCH; idx += 64 * NW) {
+    const int r = idx / KCH, c = idx % KCH;
+    int gr = tile * RT + r;
+    if (gr >= p.rows_total) gr = tile * RT;
     const int j = gr / p.group, h = kvh * p.group + gr % p.group;
-    const qconst_t* q0 = (const qconst_t*)((const uint8_t*)p.q +
-                                           ((((int64_t)b * p.q_len + j) * p.num_q_heads + h) * DK) * ES);
-#pragma unroll
-    for (int r = 0; r < RT; ++r) qrow[r] = q0 + r * (KRB / 4);
-  } else {
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      int gr = tile * RT + r;
-      if (gr >= p.rows_total) gr = tile * RT;
-      const int j = gr / p.group, h = kvh * p.group + gr % p.group;
-      qrow[r] = (const qconst_t*)((const uint8_t*)p.q +
-                                  ((((int64_t)b * p.q_len + j) * p.num_q_heads + h) * DK) * ES);
-    }
+    const uint4* src = (const uint4*)((const uint8_t*)p.q +
+                                      ((((int64_t)b * p.q_len + j) * p.num_q_heads + h) * DK) * ES);
+    *(uint4*)(q_lds + r * KRB + c * 16) = src[c];
   }
+  __syncthreads();
 
   float m[RT], l[RT], acc[RT][VE];
 #pragma unroll
@@ -204,15 +199,14 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
     // An opaque per-block offset keeps the compiler from hoisting every
     // query chunk of every row out of the block loop at once.
     uint32_t qoff = 0;
-    asm volatile("" : "+s"(qoff));
+    asm volatile("" : "+v"(qoff));
     float sc[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) sc[r] = 0.f;
     auto dot_chunk = [&](const uint4 kc, int c) {
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
-        const qconst_t* qw = qrow[r] + (qoff + c) * 4;
-        const uint4 qc = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+        const uint4 qc = *(const uint4*)(q_lds + qoff + r * KRB + c * 16);
         if constexpr (DTYPE == 0) {
           sc[r] = fmaf(__builtin_bit_cast(float, qc.x), __builtin_bit_cast(float, kc.x), sc[r]);
           sc[r] = fmaf(__builtin_bit_cast(float, qc.y), __builtin_bit_cast(float, kc.y), sc[r]);
@@ -354,7 +348,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
     float M = kNegInf;
 #pragma unroll
     for (int k = 0; k < 4 * NW; ++k) {
-      const float* ml = (const float*)(smem + (k >> 2) * C::WAVE_B) + 4 * RT * DV;
+      const float* ml = (const float*)(smem + C::QB + (k >> 2) * C::WAVE_B) + 4 * RT * DV;
       M = fmaxf(M, ml[(k & 3) * RT + r]);
     }
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -364,7 +358,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
       float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int k = 0; k < 4 * NW; ++k) {
-        const float* base = (const float*)(smem + (k >> 2) * C::WAVE_B);
+        const float* base = (const float*)(smem + C::QB + (k >> 2) * C::WAVE_B);
         const float* ml = base + 4 * RT * DV;
         const float f = fast_exp2(ml[(k & 3) * RT + r] - M);
         den += f * ml[4 * RT + (k & 3) * RT + r];
@@ -392,13 +386,12 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
 
 struct Entry {
   int dtype, dk, dv, rt, nw;
-  void (*fn[2])(Stage1Params);  // [q rows contiguous]
+  void (*fn)(Stage1Params);
 };
 
 template <int DTYPE, int DK, int DV, int RT, int NW = 4>
 constexpr Entry entry() {
-  return {DTYPE, DK, DV, RT, NW, {&stage1_valu_kernel<DTYPE, DK, DV, RT, NW, false>,
-                                  &stage1_valu_kernel<DTYPE, DK, DV, RT, NW, true>}};
+  return {DTYPE, DK, DV, RT, NW, &stage1_valu_kernel<DTYPE, DK, DV, RT, NW>};
 }
 
 constexpr Entry kTable[] = {
@@ -420,10 +413,10 @@ bool stage1_valu_supported(int dtype, int dk, int dv, int rows_per_wg) {
   return find(dtype, dk, dv, rows_per_wg) != nullptr;
 }
 
-hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, bool q_contig, hipStream_t st) {
+hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, hipStream_t st) {
   const Entry* e = find(dtype, dk, dv, p.rows_per_wg);
   if (!e) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(e->fn[q_contig ? 1 : 0], dim3(p.num_wgs), dim3(64 * e->nw), 0, st, p);
+  hipLaunchKernelGGL(e->fn, dim3(p.num_wgs), dim3(64 * e->nw), 0, st, p);
   return hipGetLastError();
 }
 
