@@ -96,7 +96,7 @@ typedef struct attn_decode_desc {
   int32_t head_dim_qk;        /* Dk */
   int32_t head_dim_v;         /* Dv (<= Dk when v_aliases_k) */
   int32_t page_size;          /* P keys per page, a power of two */
-  int32_t max_pages_per_req;  /* page_table row length */
+  int32_t max_pages_per_req;  /* page_table row length; max_pages_per_req * page_size <= 2^30 */
   int32_t dtype;              /* attn_dtype of q, K, V and out */
   int32_t causal;             /* 1: bottom-right causal among the q_len rows */
   int32_t v_aliases_k;        /* 1: V = K[..., :Dv] (MLA latent cache) */

@@ -5,14 +5,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.h"
+
 namespace splitkv {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// Read-only words in the constant address space (uniform loads from it
-// compile to s_load).
-typedef const __attribute__((address_space(4))) uint32_t qconst_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -147,14 +146,25 @@ __device__ __forceinline__ void store_out4(void* out, int dtype, int64_t off, fl
 }
 
 // Split rule: split s of S over ctx keys, chunk = A * ceil(ceil(ctx / S) / A).
-__device__ __forceinline__ void split_range(int ctx, int S, int A, int s, int& beg, int& end) {
-  int per = (ctx + S - 1) / S;
-  int chunk = ((per + A - 1) / A) * A;
-  if (chunk <= 0) chunk = A;
+__device__ __forceinline__ void split_range(int ctx, int S, FastDiv fd_S, int align_shift, int s, int& beg,
+                                            int& end) {
+  const int per = (int)fdiv((uint32_t)(ctx + S - 1), fd_S);
+  int chunk = ((per + (1 << align_shift) - 1) >> align_shift) << align_shift;
+  if (chunk <= 0) chunk = 1 << align_shift;
   long long b = (long long)s * chunk;
   long long e = b + chunk;
   beg = (int)(b < ctx ? b : ctx);
   end = (int)(e < ctx ? e : ctx);
+}
+
+// Workgroup id -> (head tile, KV head, request, split), fastest first.
+struct WgCoord {
+  int tile, kvh, b, s;
+};
+__device__ __forceinline__ WgCoord wg_coord(uint32_t lid, FastDiv fd_tiles, int tiles, FastDiv fd_kvh, int kvhs,
+                                            FastDiv fd_batch, int batch) {
+  const uint32_t q1 = fdiv(lid, fd_tiles), q2 = fdiv(q1, fd_kvh), q3 = fdiv(q2, fd_batch);
+  return WgCoord{(int)(lid - q1 * tiles), (int)(q1 - q2 * kvhs), (int)(q2 - q3 * batch), (int)q3};
 }
 
 // Workgroup order.  The dispatcher hands workgroup p to XCD p % 8; with the

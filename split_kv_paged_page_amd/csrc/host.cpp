@@ -53,6 +53,11 @@ attn_status check_desc(const attn_decode_desc* d) {
   if (d->dtype != ATTN_F32 && d->dtype != ATTN_BF16) return fail(ATTN_EINVAL, "unknown dtype %d", d->dtype);
   if (d->page_size & (d->page_size - 1))
     return fail(ATTN_EUNSUPPORTED, "page_size %d is not a power of two", d->page_size);
+  // Kernels divide context lengths and row indices as 31-bit values.
+  if ((int64_t)d->max_pages_per_req * d->page_size > (int64_t(1) << 30))
+    return fail(ATTN_EINVAL, "max_pages_per_req * page_size exceeds 2^30 keys");
+  if ((int64_t)d->batch * d->q_len * d->num_q_heads * ((d->head_dim_v + 3) / 4) >= (int64_t(1) << 31))
+    return fail(ATTN_EINVAL, "batch * q_len * num_q_heads * head_dim_v / 4 must stay below 2^31");
   if (d->causal != 0 && d->causal != 1) return fail(ATTN_EINVAL, "causal must be 0 or 1");
   if (d->v_aliases_k != 0 && d->v_aliases_k != 1) return fail(ATTN_EINVAL, "v_aliases_k must be 0 or 1");
   if (d->reserved != 0) return fail(ATTN_EINVAL, "reserved must be 0");
@@ -159,6 +164,13 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   p.causal = d.causal;
   p.num_splits = S;
   p.split_align = plan->split_align;
+  p.align_shift = 0;
+  while ((1 << p.align_shift) < p.split_align) ++p.align_shift;
+  p.fd_tiles = splitkv::make_fastdiv((uint32_t)plan->head_tiles);
+  p.fd_kvh = splitkv::make_fastdiv((uint32_t)d.num_kv_heads);
+  p.fd_batch = splitkv::make_fastdiv((uint32_t)d.batch);
+  p.fd_splits = splitkv::make_fastdiv((uint32_t)S);
+  p.fd_group = splitkv::make_fastdiv((uint32_t)(d.num_q_heads / d.num_kv_heads));
   p.rows_total = p.group * d.q_len;
   p.rows_per_wg = plan->rows_per_wg;
   p.head_tiles = plan->head_tiles;
@@ -200,6 +212,7 @@ attn_status enqueue_stage2(const attn_decode_plan_t* plan, int S, const void* ws
   p.num_splits = S;
   p.head_dim_v = d.head_dim_v;
   p.tiles = pick_stage2_tiles(p.rows, d.head_dim_v, !(plan->flags & ATTN_PLAN_NO_STAGE2_TILING));
+  p.fd_cols = splitkv::make_fastdiv((uint32_t)(d.head_dim_v / 4));
   hipError_t e = splitkv::launch_stage2(p, d.dtype, st);
   if (e != hipSuccess) return hip_fail(e, "stage-2 launch");
   return ATTN_OK;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.h"
+
 namespace splitkv {
 
 struct Stage1Params {
@@ -29,6 +31,10 @@ struct Stage1Params {
   // instead of partials (identical bits to merging one split).
   void* out;              // null: write partials
   float* lse_out;         // optional with out
+  // Divisors of the workgroup-id decomposition, the split rule and the row
+  // index (see fastdiv.h); split_align = 1 << align_shift.
+  FastDiv fd_tiles, fd_kvh, fd_batch, fd_splits, fd_group;
+  int32_t align_shift;
 };
 
 struct Stage2Params {
@@ -40,6 +46,7 @@ struct Stage2Params {
   int32_t num_splits;
   int32_t head_dim_v;
   int32_t tiles;          // Dv slices per row
+  FastDiv fd_cols;        // head_dim_v / 4 (row-major merge)
 };
 
 // Stage-1 launchers; return false when no kernel exists for the shape.

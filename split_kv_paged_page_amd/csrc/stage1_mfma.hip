@@ -153,24 +153,20 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   auto tile_k = [&](int buf) { return smem + (kw * C::NBUF + buf) * C::TILE; };
   auto tile_v = [&](int buf) { return VALIAS ? tile_k(buf) : tile_k(buf) + C::KTILE; };
 
-  int lid = logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap);
-  const int tile = lid % p.head_tiles;
-  lid /= p.head_tiles;
-  const int kvh = lid % p.num_kv_heads;
-  lid /= p.num_kv_heads;
-  const int b = lid % p.batch;
-  const int s = lid / p.batch;
+  const WgCoord wc = wg_coord((uint32_t)logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap), p.fd_tiles, p.head_tiles,
+                              p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch);
+  const int tile = wc.tile, kvh = wc.kvh, b = wc.b, s = wc.s;
 
   const int L = p.ctx[b];
   int sb, se;
-  split_range(L, p.num_splits, p.split_align, s, sb, se);
+  split_range(L, p.num_splits, p.fd_splits, p.align_shift, s, sb, se);
 
   // This lane's query row and its visible end.
   const int gr = (tile * RW + rw) * 16 + n;
   const bool row_ok = gr < p.rows_total;
   int row_end = sb;
   if (row_ok) {
-    const int j = gr / p.group;
+    const int j = (int)fdiv((uint32_t)gr, p.fd_group);
     const int nv = p.causal ? L - p.q_len + 1 + j : L;
     row_end = nv < se ? nv : se;
     if (row_end < sb) row_end = sb;
@@ -182,7 +178,7 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   if (last_row >= p.rows_total) last_row = p.rows_total - 1;
   int end_max = sb;
   {
-    const int j = last_row / p.group;
+    const int j = (int)fdiv((uint32_t)last_row, p.fd_group);
     const int nv = p.causal ? L - p.q_len + 1 + j : L;
     end_max = nv < se ? nv : se;
     if (end_max < sb) end_max = sb;
@@ -200,7 +196,7 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   bf16x8_t qb[C::KK];
   {
     const int qr = row_ok ? gr : first_row;
-    const int j = qr / p.group, h = kvh * p.group + qr % p.group;
+    const int j = (int)fdiv((uint32_t)qr, p.fd_group), h = kvh * p.group + qr - j * p.group;
     const uint4* qrow = (const uint4*)((const uint16_t*)p.q + (((int64_t)b * p.q_len + j) * p.num_q_heads + h) * DK);
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) qb[kk] = __builtin_bit_cast(bf16x8_t, qrow[kk * 4 + g]);
@@ -486,7 +482,7 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
 
   l = sum_xor32(sum_xor16(l));
   auto write_row = [&](int grr, int d, float4 o, float lse) {
-    const int j = grr / p.group, h = kvh * p.group + grr % p.group;
+    const int j = (int)fdiv((uint32_t)grr, p.fd_group), h = kvh * p.group + grr - j * p.group;
     const int64_t row = ((int64_t)b * p.q_len + j) * p.num_q_heads + h;
     if (p.out) {
       store_out4(p.out, 1, row * DV + d, o);

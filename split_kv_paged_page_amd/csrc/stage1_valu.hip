@@ -75,17 +75,13 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
   const int x = lane & 15;
   uint8_t* wave_lds = smem + C::QB + wave * C::WAVE_B;
 
-  int lid = logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap);
-  const int tile = lid % p.head_tiles;
-  lid /= p.head_tiles;
-  const int kvh = lid % p.num_kv_heads;
-  lid /= p.num_kv_heads;
-  const int b = lid % p.batch;
-  const int s = lid / p.batch;
+  const WgCoord wc = wg_coord((uint32_t)logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap), p.fd_tiles, p.head_tiles,
+                              p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch);
+  const int tile = wc.tile, kvh = wc.kvh, b = wc.b, s = wc.s;
 
   const int L = p.ctx[b];
   int sb, se;
-  split_range(L, p.num_splits, p.split_align, s, sb, se);
+  split_range(L, p.num_splits, p.fd_splits, p.align_shift, s, sb, se);
 
   int row_end[RT];
   int end_max = sb;
@@ -94,7 +90,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
     const int gr = tile * RT + r;
     int e = sb;
     if (gr < p.rows_total) {
-      const int j = gr / p.group;
+      const int j = (int)fdiv((uint32_t)gr, p.fd_group);
       const int n = p.causal ? L - p.q_len + 1 + j : L;
       e = n < se ? n : se;
       if (e < sb) e = sb;
@@ -129,7 +125,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
     const int r = idx / KCH, c = idx % KCH;
     int gr = tile * RT + r;
     if (gr >= p.rows_total) gr = tile * RT;
-    const int j = gr / p.group, h = kvh * p.group + gr % p.group;
+    const int j = (int)fdiv((uint32_t)gr, p.fd_group), h = kvh * p.group + gr - j * p.group;
     const uint4* src = (const uint4*)((const uint8_t*)p.q +
                                       ((((int64_t)b * p.q_len + j) * p.num_q_heads + h) * DK) * ES);
     *(uint4*)(q_lds + r * KRB + c * 16) = src[c];
@@ -372,7 +368,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
       o = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
       lse = (M + __log2f(den)) * kLn2;
     }
-    const int j = gr / p.group, h = kvh * p.group + gr % p.group;
+    const int j = (int)fdiv((uint32_t)gr, p.fd_group), h = kvh * p.group + gr - j * p.group;
     const int64_t row = ((int64_t)b * p.q_len + j) * p.num_q_heads + h;
     if (p.out) {
       store_out4(p.out, DTYPE, row * DV + d, o);

@@ -136,10 +136,11 @@ template <int DTYPE>
 __global__ __launch_bounds__(kThreads) void stage2_rows_kernel(Stage2Params p) {
   const int Dv = p.head_dim_v;
   const int cols = Dv / 4;
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t row = idx / cols;
-  if (row >= p.rows) return;
-  const int c = (int)(idx % cols);
+  const uint32_t idx = blockIdx.x * kThreads + threadIdx.x;   // rows * cols < 2^31 (host-checked)
+  const uint32_t rq = fdiv(idx, p.fd_cols);
+  if ((int)rq >= p.rows) return;
+  const int64_t row = rq;
+  const int c = (int)(idx - rq * cols);
   const int S = p.num_splits;
   const float* lse_row = p.lse_part + row * S;
   const float* base = p.o_part + row * S * Dv + c * 4;

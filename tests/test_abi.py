@@ -152,6 +152,17 @@ def test_plan_rejects_page_size_not_power_of_two():
     assert ei.value.status == sk.ATTN_EUNSUPPORTED
 
 
+def test_plan_rejects_index_ranges_past_31_bits():
+    # the kernels divide context lengths and row indices as 31-bit values
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_plan(desc(P=1, maxp=(1 << 30) + 1), 1024, 0)
+    assert ei.value.status == sk.ATTN_EINVAL
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_plan(desc(B=1 << 20, Hq=512, Hkv=1, maxp=64), 1024, 0)
+    assert ei.value.status == sk.ATTN_EINVAL
+    sk.attn_decode_plan(desc(P=1, maxp=1 << 30), 1024, 0)
+
+
 def test_plan_rejects_misaligned_stride():
     d = desc()
     d.k_stride_tok = 129          # 258-byte rows break 16-byte alignment
