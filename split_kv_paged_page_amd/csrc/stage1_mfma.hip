@@ -4,12 +4,12 @@
 // bh16 / bh64 regimes) or a wide GQA group with draft tokens.
 //
 // Each wave owns 16 query rows.  A workgroup has RW x KW waves: RW 16-row
-// tiles that share each K block through LDS (double-buffered, one barrier
-// per block; the next block's loads overlap the current block's compute) and
-// KW key streams that take the split's 32-key blocks in turn with their own
-// running max / sum / accumulators, merged at the end.  One tile and four
-// streams suit 16 rows per KV head; four tiles and one stream suit 64 or
-// more (the wide MLA shape reads each K block once per 64 rows).
+// tiles that share each K/V block through a ring of four LDS tiles (three
+// blocks in flight, one barrier per block) or KW key streams that take the
+// split's 32-key blocks in turn with their own tile and running max / sum /
+// accumulators, merged at the end.  One tile and four streams suit 16 rows
+// per KV head; two or four tiles and one stream suit 32 or 64+ rows (draft
+// groups, the wide MLA shape), reading each block once per 32 or 64 rows.
 // Per block:
 //   * page walk: lane k < 32 looks up key k's page; keys past the visible end
 //     clamp to the last visible key (weight 0 later);
@@ -565,6 +565,7 @@ constexpr Entry kTable[] = {
     {576, 512, true, 1, 4, &stage1_mfma_kernel<576, 512, true, 1, 4>},
     {576, 512, true, 4, 1, &stage1_mfma_kernel<576, 512, true, 4, 1>},
     {256, 256, false, 1, 4, &stage1_mfma_kernel<256, 256, false, 1, 4>},
+    {256, 256, false, 2, 1, &stage1_mfma_kernel<256, 256, false, 2, 1>},
     {128, 128, false, 1, 4, &stage1_mfma_kernel<128, 128, false, 1, 4>},
 };
 
@@ -581,9 +582,10 @@ bool stage1_mfma_supported(int dtype, int dk, int dv, bool v_aliases_k) {
 }
 
 int stage1_mfma_row_tiles(int dk, int dv, bool v_aliases_k, int rows) {
-  // Several 16-row tiles share one K stream only when there are enough rows
-  // to fill all of them (the wide MLA shape); otherwise one tile per wave.
-  for (int rw : {4}) {
+  // Several 16-row tiles share one K/V stream through the LDS ring when
+  // there are enough rows to fill all of them (the wide MLA shape, 32-row
+  // draft groups); otherwise one tile per wave with four key streams.
+  for (int rw : {4, 2}) {
     if (rows >= 16 * rw && find(dk, dv, v_aliases_k, rw)) return rw;
   }
   return 1;
