@@ -216,7 +216,7 @@ def main():
                    "page_size": w.page_size, "context": (w.context_lens[0] if len(set(w.context_lens)) == 1
                                                         else list(w.context_lens)),
                    "num_splits": S, "rows_per_wg": plan.rows_per_wg, "head_tiles": plan.head_tiles,
-                   "stage2_tiles": plan.stage2_tiles, "xcd_remap": plan.xcd_remap, "replicas": R,
+                   "stage1_waves": plan.stage1_waves, "xcd_remap": plan.xcd_remap, "replicas": R,
                    "kv_bytes_per_op": kv_bytes, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "stage1", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,

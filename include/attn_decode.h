@@ -77,14 +77,15 @@ typedef enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
 enum {
   ATTN_PLAN_POLICY_P2 = 1,          /* split count = max(1, 256 / batch), the policy the
                                        aiter PR's per-lever table was measured at */
-  ATTN_PLAN_NO_XCD_REMAP = 2,       /* keep the plain (split-minor) workgroup order */
-  ATTN_PLAN_NO_STAGE2_TILING = 4    /* one stage-2 workgroup per query row */
+  ATTN_PLAN_NO_XCD_REMAP = 2        /* keep the plain (split-minor) workgroup order */
 };
 
 /* Kernel families the planner picks from. */
 enum {
-  ATTN_VARIANT_VALU = 1,            /* vector-ALU stage 1 (fewer than 16 rows per KV head) */
-  ATTN_VARIANT_MFMA = 2             /* matrix-core stage 1 (16 or more rows per KV head) */
+  ATTN_VARIANT_VALU = 1,            /* vector-ALU stage 1 (fp32; bf16 with fewer than 8 rows
+                                       per KV head or head dims without a matrix-core kernel) */
+  ATTN_VARIANT_MFMA = 2             /* matrix-core stage 1 (bf16, 8 or more rows per KV head,
+                                       head dims 128/128, 256/256 or 576/512 with V = K[:512]) */
 };
 
 /* Shape and layout of one decode call; filled by the caller. */
@@ -116,8 +117,7 @@ typedef struct attn_decode_plan_t {
   int32_t variant;            /* ATTN_VARIANT_* */
   int32_t rows_per_wg;        /* query rows one stage-1 workgroup scores */
   int32_t head_tiles;         /* stage-1 workgroups per (request, KV head, split) */
-  int32_t stage2_tiles;       /* Dv slices per query row of the stage-2 merge when it runs
-                                 more than 16 splits (16 or fewer: one thread per 4 dims) */
+  int32_t stage1_waves;       /* wavefronts per stage-1 workgroup */
   int32_t xcd_remap;          /* 1: split-major, XCD-contiguous workgroup order */
   int32_t flags;              /* ATTN_PLAN_* given to attn_decode_plan */
   int64_t workspace_bytes;    /* bytes the caller must provide at max_splits */
@@ -128,8 +128,7 @@ typedef struct attn_decode_plan_t {
  * Plan a decode call.  Pure host function: checks the descriptor, picks the
  * kernel variant, the split count S (num_splits > 0 forces it; 0 lets the
  * policy choose so that about 256 CUs' worth of stage-1 workgroups exist,
- * aiter PR #4758, Motivation), the workgroup order and the stage-2 tiling,
- * and sizes the workspace for max(S, num_splits) splits.
+ * aiter PR #4758, Motivation) and the workgroup order, and sizes the workspace for max(S, num_splits) splits.
  * Returns ATTN_EINVAL / ATTN_EUNSUPPORTED on a bad or unsupported shape.
  */
 attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_len,

@@ -19,7 +19,6 @@ ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP = range(5)
 ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_PLAN_POLICY_P2 = 1
 ATTN_PLAN_NO_XCD_REMAP = 2
-ATTN_PLAN_NO_STAGE2_TILING = 4
 ATTN_VARIANT_VALU, ATTN_VARIANT_MFMA = 1, 2
 
 EXPORTED = ["attn_decode_plan", "attn_decode_run", "attn_decode_partials", "attn_decode_merge",
@@ -47,7 +46,7 @@ class AttnDecodeDesc(ctypes.Structure):
 class AttnDecodePlan(ctypes.Structure):
     _fields_ = [("desc", AttnDecodeDesc)] + [(n, ctypes.c_int32) for n in (
         "max_context_len", "num_splits", "max_splits", "split_align", "variant", "rows_per_wg",
-        "head_tiles", "stage2_tiles", "xcd_remap", "flags")] + \
+        "head_tiles", "stage1_waves", "xcd_remap", "flags")] + \
         [("workspace_bytes", ctypes.c_int64), ("key", ctypes.c_uint64)]
 
     def as_dict(self) -> dict:

@@ -27,7 +27,7 @@ attn_status hip_fail(hipError_t e, const char* what) {
 
 constexpr int kSplitAlign = 64;   // keys per stage-1 block and split granule
 constexpr int kNumCu = 256;       // MI355X compute units
-constexpr int kMaxSplits = 4096;  // stage 2 keeps one weight per split in LDS
+constexpr int kMaxSplits = 4096;  // far above any useful split count; bounds the workspace
 
 uint64_t fnv1a(const void* p, size_t n, uint64_t h = 1469598103934665603ull) {
   const unsigned char* c = static_cast<const unsigned char*>(p);
@@ -94,16 +94,6 @@ int pick_rows_per_wg(int dtype, int dk, int dv, int rows) {
   for (int rt : {4, 8, 16})
     if (splitkv::stage1_valu_supported(dtype, dk, dv, rt)) best = rt;
   return best;
-}
-
-int pick_stage2_tiles(int rows2, int dv, bool allow) {
-  if (!allow) return 1;
-  // Slice the head dim only while the merge grid would leave CUs idle
-  // (aiter PR #4758, Technical Details item 3: up to 8 ways, fewer when the
-  // head dim does not divide evenly).
-  int t = 1;
-  while (t < 8 && rows2 * (t * 2) <= kNumCu && dv % (t * 2) == 0 && (dv / (t * 2)) % 4 == 0) t *= 2;
-  return t;
 }
 
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
@@ -184,9 +174,10 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   p.vs_page = d.v_stride_page;
   p.vs_head = d.v_stride_head;
   p.vs_tok = d.v_stride_tok;
+  const int rw = plan->rows_per_wg / 16;
   hipError_t e = plan->variant == ATTN_VARIANT_MFMA
                      ? splitkv::launch_stage1_mfma(p, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0,
-                                                   plan->rows_per_wg / 16, st)
+                                                   splitkv::MfmaShape{rw, plan->stage1_waves / rw}, st)
                      : splitkv::launch_stage1_valu(p, d.dtype, d.head_dim_qk, d.head_dim_v, st);
   if (e != hipSuccess) return hip_fail(e, "stage-1 launch");
   return ATTN_OK;
@@ -211,7 +202,6 @@ attn_status enqueue_stage2(const attn_decode_plan_t* plan, int S, const void* ws
   p.rows = d.batch * d.q_len * d.num_q_heads;
   p.num_splits = S;
   p.head_dim_v = d.head_dim_v;
-  p.tiles = pick_stage2_tiles(p.rows, d.head_dim_v, !(plan->flags & ATTN_PLAN_NO_STAGE2_TILING));
   p.fd_cols = splitkv::make_fastdiv((uint32_t)(d.head_dim_v / 4));
   hipError_t e = splitkv::launch_stage2(p, d.dtype, st);
   if (e != hipSuccess) return hip_fail(e, "stage-2 launch");
@@ -234,7 +224,7 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
     return fail(ATTN_EINVAL, "max_context_len %d exceeds max_pages_per_req * page_size", max_context_len);
   if (num_splits < 0 || num_splits > kMaxSplits)
     return fail(ATTN_EINVAL, "num_splits must be in [0, %d]", kMaxSplits);
-  if (flags & ~(ATTN_PLAN_POLICY_P2 | ATTN_PLAN_NO_XCD_REMAP | ATTN_PLAN_NO_STAGE2_TILING))
+  if (flags & ~(ATTN_PLAN_POLICY_P2 | ATTN_PLAN_NO_XCD_REMAP))
     return fail(ATTN_EINVAL, "unknown plan flags 0x%x", flags);
 
   const attn_decode_desc& d = *desc;
@@ -245,11 +235,16 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
   p.split_align = kSplitAlign;
   p.flags = flags;
   p.xcd_remap = (flags & ATTN_PLAN_NO_XCD_REMAP) ? 0 : 1;
-  // Matrix cores only where 16 or more query rows share a KV head: below
-  // that Q.K and P.V are not dense enough for a 16-row MFMA tile.
-  if (rows >= 16 && splitkv::stage1_mfma_supported(d.dtype, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0)) {
+  // Matrix cores where 8 or more query rows share a KV head (bf16, head dims
+  // with a matrix-core kernel): a 16-row tile is then at least half full, and
+  // its Q.K and P.V cost a fraction of the vector-ALU work per key.  Fewer
+  // rows, fp32 and other head dims stay on the vector ALUs.
+  const splitkv::MfmaShape ms =
+      splitkv::stage1_mfma_shape(d.dtype, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0, rows);
+  if (ms.rw > 0) {
     p.variant = ATTN_VARIANT_MFMA;
-    p.rows_per_wg = 16 * splitkv::stage1_mfma_row_tiles(d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0, rows);
+    p.rows_per_wg = 16 * ms.rw;
+    p.stage1_waves = ms.rw * ms.kw;
   } else {
     const int rt = pick_rows_per_wg(d.dtype, d.head_dim_qk, d.head_dim_v, rows);
     if (!rt)
@@ -257,6 +252,7 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
                   d.head_dim_v);
     p.variant = ATTN_VARIANT_VALU;
     p.rows_per_wg = rt;
+    p.stage1_waves = 4;
   }
   p.head_tiles = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
 
@@ -273,10 +269,11 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
     S = kNumCu / d.batch;
     if (S < 1) S = 1;
   } else {
-    // VALU workgroups fit two per CU; MFMA workgroups (large LDS tiles, a
-    // full register file per wave) one per CU: aim for one full round.
+    // VALU workgroups and lone MFMA waves (a 48 KB ring) fit two per CU;
+    // larger MFMA workgroups (144-148 KB of LDS tiles, or a full register
+    // file per wave) one per CU: aim for one full round.
     const int per_split = d.batch * d.num_kv_heads * p.head_tiles;
-    const int target = p.variant == ATTN_VARIANT_MFMA ? kNumCu : 2 * kNumCu;
+    const int target = p.variant == ATTN_VARIANT_MFMA && p.stage1_waves > 1 ? kNumCu : 2 * kNumCu;
     S = target / per_split;
     if (S > blocks) S = blocks;
     if (S < 1) S = 1;
@@ -284,9 +281,7 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
   if (S > kMaxSplits) S = kMaxSplits;
   p.num_splits = S;
   p.max_splits = S;
-  p.stage2_tiles = pick_stage2_tiles(d.batch * d.q_len * d.num_q_heads, d.head_dim_v,
-                                     !(flags & ATTN_PLAN_NO_STAGE2_TILING));
-  if (!splitkv::stage2_supported(d.dtype, d.head_dim_v, p.stage2_tiles))
+  if (!splitkv::stage2_supported(d.dtype, d.head_dim_v))
     return fail(ATTN_EUNSUPPORTED, "no stage-2 kernel for head_dim_v %d", d.head_dim_v);
   int64_t bytes;
   layout(&p, p.max_splits, nullptr, nullptr, &bytes);
@@ -296,7 +291,7 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
   // missed the batch baked into the binary).
   uint64_t h = fnv1a(&p.desc, sizeof(p.desc));
   const int32_t fields[] = {p.max_context_len, p.num_splits, p.max_splits, p.split_align, p.variant,
-                            p.rows_per_wg,     p.head_tiles, p.stage2_tiles, p.xcd_remap, p.flags};
+                            p.rows_per_wg,     p.head_tiles, p.stage1_waves, p.xcd_remap, p.flags};
   h = fnv1a(fields, sizeof(fields), h);
   p.key = h;
   *plan = p;

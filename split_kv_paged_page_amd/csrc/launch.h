@@ -45,7 +45,6 @@ struct Stage2Params {
   int32_t rows;           // B * q_len * Hq
   int32_t num_splits;
   int32_t head_dim_v;
-  int32_t tiles;          // Dv slices per row
   FastDiv fd_cols;        // head_dim_v / 4 (row-major merge)
 };
 
@@ -53,12 +52,16 @@ struct Stage2Params {
 bool stage1_valu_supported(int dtype, int dk, int dv, int rows_per_wg);
 hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, hipStream_t s);
 
-bool stage1_mfma_supported(int dtype, int dk, int dv, bool v_aliases_k);
-int stage1_mfma_row_tiles(int dk, int dv, bool v_aliases_k, int rows);
-hipError_t launch_stage1_mfma(const Stage1Params& p, int dk, int dv, bool v_aliases_k, int row_tiles,
+// Matrix-core workgroup shape: rw 16-row tiles x kw key streams ({0, 0}: no
+// matrix-core kernel for this dtype, head dims and rows per KV head).
+struct MfmaShape {
+  int rw, kw;
+};
+MfmaShape stage1_mfma_shape(int dtype, int dk, int dv, bool v_aliases_k, int rows);
+hipError_t launch_stage1_mfma(const Stage1Params& p, int dk, int dv, bool v_aliases_k, MfmaShape shape,
                               hipStream_t s);
 
-bool stage2_supported(int dtype, int dv, int tiles);
+bool stage2_supported(int dtype, int dv);
 hipError_t launch_stage2(const Stage2Params& p, int dtype, hipStream_t s);
 
 }  // namespace splitkv

@@ -1,15 +1,19 @@
 // Stage 1 of split-KV paged decode on the matrix cores (gfx950), for KV heads
-// shared by 16 or more query rows: an MLA latent head (aiter PR #4758,
+// shared by 8 or more query rows: an MLA latent head (aiter PR #4758,
 // "[Gluon][MLA] Deeper async-copy pipeline in the bh16 stage-1 decode loop",
-// bh16 / bh64 regimes) or a wide GQA group with draft tokens.
+// bh16 / bh64 regimes), a GQA group, or a wide GQA group with draft tokens.
 //
-// Each wave owns 16 query rows.  A workgroup has RW x KW waves: RW 16-row
-// tiles that share each K/V block through a ring of four LDS tiles (three
-// blocks in flight, one barrier per block) or KW key streams that take the
-// split's 32-key blocks in turn with their own tile and running max / sum /
-// accumulators, merged at the end.  One tile and four streams suit 16 rows
-// per KV head; two or four tiles and one stream suit 32 or 64+ rows (draft
-// groups, the wide MLA shape), reading each block once per 32 or 64 rows.
+// Each wave owns 16 query rows (a group of 8 fills half of the tile; the
+// matrix cores have throughput to spare at decode's few flops per byte).  A
+// workgroup has RW x KW waves: RW 16-row tiles that share each K/V block
+// through a ring of LDS tiles (one barrier per block), or KW key streams that
+// take the split's 32-key blocks in turn with their own tile and running max
+// / sum / accumulators, merged at the end.  Shapes, by rows per KV head:
+//   * 64+ (wide MLA), 32 (draft groups): 4 or 2 tiles on a ring of 4 (three
+//     blocks in flight), each block read once per 64 or 32 rows;
+//   * 16 (MLA bh16): one tile, four key streams, load -> wait -> compute;
+//   * 8-15 (GQA): one wave alone on a ring of 3 (two blocks in flight),
+//     48 KB of LDS at head dim 128, two or three workgroups per CU.
 // Per block:
 //   * page walk: lane k < 32 looks up key k's page; keys past the visible end
 //     clamp to the last visible key (weight 0 later);
@@ -55,7 +59,9 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 template <int DK, int DV, bool VALIAS, int RW, int KW>
 struct MCfg {
   static constexpr int NW = RW * KW;               // waves: RW row tiles x KW key streams
-  static constexpr int NBUF = RW > 1 ? 4 : 1;      // shared tiles: a ring of 4 (3 blocks in flight)
+  // Ring depth: 4 tiles for shared row tiles, 3 for a lone wave (measured
+  // faster than 4 there), none for key streams (one tile each).
+  static constexpr int NBUF = RW > 1 ? 4 : KW == 1 ? 3 : 1;
   static constexpr int KCH = DK * 2 / 16;          // 16-byte chunks of a K row
   static constexpr int VCH = DV * 2 / 16;          // 16-byte chunks of a V row
   static constexpr int KK = DK / 32;               // Q.K MFMA steps
@@ -66,7 +72,7 @@ struct MCfg {
   static constexpr int VTILE = VALIAS ? 0 : VCH * 32 * 16;
   static constexpr int TILE = ((KTILE + VTILE) + 255) / 256 * 256;
   static constexpr int TILES = KW * NBUF * TILE;
-  static constexpr int PIDS = RW > 1 ? NW * NBUF * 256 : 0;  // per-wave page-id ring (shared tiles only)
+  static constexpr int PIDS = NBUF > 1 ? NW * NBUF * 256 : 0;  // per-wave page-id ring (ring path only)
   static constexpr int PART = 16 * DV * 4 + 2 * 16 * 4;  // merge state: acc [16][DV], m[16], l[16]
   static constexpr int PARTS = KW > 1 ? NW * PART : 0;   // only key streams need merging
   static constexpr int SMEM = TILES + PIDS > PARTS ? TILES + PIDS : PARTS;
@@ -75,7 +81,7 @@ struct MCfg {
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   static_assert(KINS % RW == 0 && VINS % RW == 0, "DMA instructions split evenly over the row tiles");
   static_assert(RW == 1 || KW == 1, "shared tiles carry one key stream");
-  static constexpr int MINE = RW > 1 ? (KINS + VINS) / RW : 0;  // DMA instructions per wave per block
+  static constexpr int MINE = NBUF > 1 ? (KINS + VINS) / RW : 0;  // DMA instructions per wave per block
 };
 
 // 16-byte slot of chunk c of key k (k < 32) in a tile.
@@ -414,11 +420,11 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
       __builtin_amdgcn_wave_barrier();
       return 0;
     });
-  } else if (nit > 0) {    // RW waves share a ring of NBUF tiles; D = NBUF - 1 blocks are in flight
-    // while one is computed.  Iteration it waits for block it, meets the
-    // other waves (block it is then in LDS, and the buffer block it + D
-    // reuses is no longer read), loads the page ids of block it + 2D - 1 and
-    // issues block it + D.  Page ids are thus loaded D - 1 blocks before their
+  } else if (nit > 0) {    // RW waves (or one) share a ring of NBUF tiles; D = NBUF - 1 blocks are in
+    // flight while one is computed.  Iteration it waits for block it, meets
+    // the other waves (block it is then in LDS, and the buffer block it + D
+    // reuses is no longer read), loads the page ids of block it + 2D and
+    // issues block it + D.  Page ids are thus loaded D blocks before their
     // DMA, so the compiler's wait for them never drains the DMA queue, and
     // the explicit wait for block it counts exactly the loads issued after
     // it: D - 1 x (one page-id load + this wave's DMAs).  Near the end of the
@@ -558,45 +564,39 @@ struct Entry {
   int dk, dv;
   bool valias;
   int rw, kw;
+  int min_rows;   // rows per KV head this shape needs
   void (*fn)(Stage1Params);
 };
 
+// Per head-dim pair, in order of preference: the first entry whose min_rows
+// the group reaches is used.
 constexpr Entry kTable[] = {
-    {576, 512, true, 1, 4, &stage1_mfma_kernel<576, 512, true, 1, 4>},
-    {576, 512, true, 4, 1, &stage1_mfma_kernel<576, 512, true, 4, 1>},
-    {256, 256, false, 1, 4, &stage1_mfma_kernel<256, 256, false, 1, 4>},
-    {256, 256, false, 2, 1, &stage1_mfma_kernel<256, 256, false, 2, 1>},
-    {128, 128, false, 1, 4, &stage1_mfma_kernel<128, 128, false, 1, 4>},
+    {576, 512, true, 4, 1, 64, &stage1_mfma_kernel<576, 512, true, 4, 1>},
+    {576, 512, true, 1, 4, 16, &stage1_mfma_kernel<576, 512, true, 1, 4>},
+    {256, 256, false, 2, 1, 32, &stage1_mfma_kernel<256, 256, false, 2, 1>},
+    {256, 256, false, 1, 4, 16, &stage1_mfma_kernel<256, 256, false, 1, 4>},
+    {128, 128, false, 1, 4, 16, &stage1_mfma_kernel<128, 128, false, 1, 4>},
+    {128, 128, false, 1, 1, 8, &stage1_mfma_kernel<128, 128, false, 1, 1>},
 };
-
-const Entry* find(int dk, int dv, bool valias, int rw) {
-  for (const Entry& e : kTable)
-    if (e.dk == dk && e.dv == dv && e.valias == valias && e.rw == rw) return &e;
-  return nullptr;
-}
 
 }  // namespace
 
-bool stage1_mfma_supported(int dtype, int dk, int dv, bool v_aliases_k) {
-  return dtype == 1 && find(dk, dv, v_aliases_k, 1) != nullptr;
+MfmaShape stage1_mfma_shape(int dtype, int dk, int dv, bool v_aliases_k, int rows) {
+  if (dtype != 1) return MfmaShape{0, 0};
+  for (const Entry& e : kTable)
+    if (e.dk == dk && e.dv == dv && e.valias == v_aliases_k && rows >= e.min_rows) return MfmaShape{e.rw, e.kw};
+  return MfmaShape{0, 0};
 }
 
-int stage1_mfma_row_tiles(int dk, int dv, bool v_aliases_k, int rows) {
-  // Several 16-row tiles share one K/V stream through the LDS ring when
-  // there are enough rows to fill all of them (the wide MLA shape, 32-row
-  // draft groups); otherwise one tile per wave with four key streams.
-  for (int rw : {4, 2}) {
-    if (rows >= 16 * rw && find(dk, dv, v_aliases_k, rw)) return rw;
-  }
-  return 1;
-}
-
-hipError_t launch_stage1_mfma(const Stage1Params& p, int dk, int dv, bool v_aliases_k, int row_tiles,
+hipError_t launch_stage1_mfma(const Stage1Params& p, int dk, int dv, bool v_aliases_k, MfmaShape sh,
                               hipStream_t st) {
-  const Entry* e = find(dk, dv, v_aliases_k, row_tiles);
-  if (!e) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(e->fn, dim3(p.num_wgs), dim3(64 * e->rw * e->kw), 0, st, p);
-  return hipGetLastError();
+  for (const Entry& e : kTable) {
+    if (e.dk == dk && e.dv == dv && e.valias == v_aliases_k && e.rw == sh.rw && e.kw == sh.kw) {
+      hipLaunchKernelGGL(e.fn, dim3(p.num_wgs), dim3(64 * e.rw * e.kw), 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace splitkv

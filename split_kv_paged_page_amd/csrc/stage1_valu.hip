@@ -3,8 +3,9 @@
 // One workgroup scores one split of one request's keys against RT query rows
 // that share a KV head (aiter PR #4758, "[Gluon][MLA] Deeper async-copy
 // pipeline in the bh16 stage-1 decode loop", Motivation: each stage-1
-// program walks its split's KV blocks).  Fewer than 16 rows per KV head are
-// too few for a dense matrix-core contraction, so this kernel stays on VALU.
+// program walks its split's KV blocks).  It serves fp32 caches, and bf16
+// groups of fewer than 8 rows per KV head (or head dims without a
+// matrix-core kernel), where a 16-row matrix-core tile would be mostly empty.
 //
 // NW waves take 64-key blocks of the split in turn, each with its own
 // running max / sum / accumulator, merged at the end.  Per wave and block:
@@ -393,7 +394,7 @@ constexpr Entry entry() {
 constexpr Entry kTable[] = {
     entry<0, 64, 64, 4>(),   entry<0, 64, 64, 8>(),   entry<0, 64, 64, 16>(),
     entry<0, 128, 128, 4>(), entry<0, 128, 128, 8>(), entry<0, 128, 128, 16>(),
-    entry<1, 128, 128, 4>(), entry<1, 128, 128, 8>(), entry<1, 128, 128, 16>(),
+    entry<1, 128, 128, 4>(), entry<1, 128, 128, 8>(),
     entry<1, 256, 256, 4>(), entry<1, 256, 256, 8>(), entry<1, 576, 512, 4>(),
 };
 

@@ -104,6 +104,28 @@ def test_default_policy_fills_the_chip():
     assert p.num_splits == 2
 
 
+def test_kernel_choice_by_rows_per_kv_head():
+    # (query heads, KV heads, q_len, head dims, dtype) -> (variant, rows per workgroup, waves)
+    V, M = sk.ATTN_VARIANT_VALU, sk.ATTN_VARIANT_MFMA
+    cases = [
+        (dict(Hq=8), (V, 4, 4)),                          # 4 rows: vector ALUs
+        (dict(Hq=12), (V, 8, 4)),                         # 6 rows
+        (dict(Hq=16), (M, 16, 1)),                        # 8 rows: one wave on a ring, half a tile
+        (dict(Hq=24), (M, 16, 1)),                        # 12 rows
+        (dict(Hq=32), (M, 16, 4)),                        # 16 rows: four key streams
+        (dict(Hq=16, dtype=sk.ATTN_F32), (V, 8, 4)),      # fp32 stays on the vector ALUs
+        (dict(Hq=64, Hkv=8, q_len=4, Dk=256, Dv=256, causal=1), (M, 32, 2)),   # 32 draft rows
+        (dict(Hq=16, Hkv=2, Dk=256, Dv=256), (V, 8, 4)),  # 8 rows at head dim 256
+    ]
+    for kw, want in cases:
+        p = sk.attn_decode_plan(desc(**kw), 4096, 0)
+        assert (p.variant, p.rows_per_wg, p.stage1_waves) == want, (kw, want)
+    p = sk.attn_decode_plan(mla_desc(48), 68000, 0)
+    assert (p.variant, p.rows_per_wg, p.stage1_waves) == (M, 16, 4)
+    p = sk.attn_decode_plan(desc(Hq=128, Hkv=1, Dk=576, Dv=512, P=1, maxp=68000, alias=1, pages=655360), 68000, 0)
+    assert (p.variant, p.rows_per_wg, p.stage1_waves) == (M, 64, 4)
+
+
 def test_plan_key_covers_shape_fields():
     # rocm-libraries PR #10102, Technical Details: two configurations that differ only in
     # batch shared a launcher-cache entry; every descriptor field must reach the key.

@@ -31,6 +31,13 @@ def small_cases():
         "mla_b48_b16": scaled("mla_b48", batch=16, context_lens=(1000,) * 16, prefix_len=700),
         "mla_wide_b4": scaled("mla_wide", context_lens=(777, 1, 300, 2049)),
         "varlen_drafts": get("varlen_drafts"),
+        # group sizes around the vector-ALU / matrix-core boundary (8 rows):
+        # 4 and 6 rows stay on the vector ALUs (bf16), 12 rows half-fill a
+        # 16-row matrix-core tile, 20 rows leave a second tile with 4 rows
+        "gqa_g4_bf16": scaled("gqa_64k", context_lens=(3000, 1, 777), num_q_heads=8, seed=22),
+        "gqa_g6_bf16": scaled("gqa_64k", context_lens=(2500, 130), num_q_heads=12, seed=23),
+        "gqa_g12_bf16": scaled("gqa_64k", context_lens=(4100, 65), num_q_heads=24, seed=24),
+        "gqa_g20_bf16": scaled("gqa_64k", context_lens=(1500, 2049), num_q_heads=40, seed=25),
     }
 
 
@@ -85,7 +92,8 @@ def test_parity_small(name):
           f"out {e_out:.2e} lse {e_lse:.2e}")
 
 
-@pytest.mark.parametrize("name", ["gqa_64k_s5000", "mla_b4_private", "mla_wide_b4", "varlen_drafts"])
+@pytest.mark.parametrize("name", ["gqa_64k_s5000", "mla_b4_private", "mla_wide_b4", "varlen_drafts",
+                                  "gqa_g4_bf16", "gqa_g12_bf16"])
 @pytest.mark.parametrize("top,q_gain", [(4.0, 1.0), (1.0, 8.0), (3.0, 4.0)])
 def test_parity_rising_and_peaked_scores(name, top, q_gain):
     # Keys scaled up along the context (and/or a peaked q) make the running
@@ -100,7 +108,8 @@ def test_parity_rising_and_peaked_scores(name, top, q_gain):
 
 
 @pytest.mark.parametrize("name,splits", [("gqa_tiny_f32", (1, 2, 4, 7, 16)),
-                                         ("gqa_64k_s5000", (1, 3, 64, 79, 200)),
+                                         ("gqa_64k_s5000", (1, 3, 64, 79, 200, 300)),
+                                         ("gqa_g6_bf16", (1, 17, 40)),
                                          ("varlen_drafts", (1, 5, 33)),
                                          ("mla_b48_b16", (2, 17))])
 def test_parity_forced_splits(name, splits):
@@ -192,8 +201,8 @@ def test_bitexact_gather_and_boundaries(name, where):
 
 
 def test_bit_identity_of_relabellings():
-    """XCD-aware order, stage-2 slicing and physical page placement change
-    no bits (aiter PR #4758, Technical Details items 2 and 3)."""
+    """XCD-aware order and physical page placement change no bits (aiter PR
+    #4758, Technical Details item 2)."""
     import split_kv_paged_page_amd as sk
     for name in ("gqa_64k_b3_ragged", "mla_b48_b16"):
         w = small_cases()[name]
@@ -201,8 +210,7 @@ def test_bit_identity_of_relabellings():
         say(f"relabel {name} default")
         a = Decode(inp).run()
         ref_out, ref_lse, ref_ws = a.out.cpu(), a.lse.cpu(), a.used_ws_bits()
-        for flags in (sk.ATTN_PLAN_NO_XCD_REMAP, sk.ATTN_PLAN_NO_STAGE2_TILING,
-                      sk.ATTN_PLAN_NO_XCD_REMAP | sk.ATTN_PLAN_NO_STAGE2_TILING):
+        for flags in (sk.ATTN_PLAN_NO_XCD_REMAP,):
             say(f"relabel {name} flags={flags}")
             bdec = Decode(inp, num_splits=a.S, flags=flags).run()
             assert torch.equal(bdec.out.cpu(), ref_out)
@@ -256,13 +264,14 @@ def test_single_split_direct_output_matches_merge(name):
     check_against_oracle(d, tol_for(w), S=1)
 
 
-@pytest.mark.parametrize("name", ["gqa_tiny_f32", "gqa_64k_s5000", "varlen_drafts"])
-def test_stage2_alone_on_oracle_partials(name):
+@pytest.mark.parametrize("name,S", [("gqa_tiny_f32", None), ("gqa_64k_s5000", None), ("gqa_64k_s5000", 300),
+                                    ("varlen_drafts", None)])
+def test_stage2_alone_on_oracle_partials(name, S):
     """Merge oracle partials (rounded to fp32) on the GPU; compare with the
     oracle's float64 merge of the same rounded partials."""
     w = small_cases()[name]
     inp = inputs(name, w)
-    d = Decode(inp, num_splits=w.num_splits or 9)
+    d = Decode(inp, num_splits=S or w.num_splits or 9)
     S = d.S
     po, pl = oracle.split_reference(inp, S)
     po32, pl32 = po.astype(np.float32), pl.astype(np.float32)
@@ -278,6 +287,46 @@ def test_stage2_alone_on_oracle_partials(name):
     tol = 1e-5 if w.kv_dtype == "f32" else 1e-2
     assert row_rel_err(d.out_f64(), mo) <= tol
     assert lse_err(d.lse_f64(), ml) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("S", [2, 16, 17, 256, 257, 700])
+def test_stage2_alone_on_random_partials(S, dtype):
+    """The merge on seeded partials of every kind the split rule can leave:
+    split log-sum-exps spread over +-20 (up to 80 apart within one row),
+    empty splits (-inf) scattered and in runs, one row with every split
+    empty.  Split counts on both sides of the two kernels' boundary (16)
+    and of the register chunk of the many-split kernel (256)."""
+    B, Hq, Hkv, D, P = 2, 16, 2, 128, 16
+    rng = np.random.default_rng(1000 + S)
+    po = rng.standard_normal((B, 1, Hq, S, D))
+    pl = rng.uniform(-20.0, 20.0, (B, 1, Hq, S))
+    pl[0, 0, 0] += np.linspace(0.0, 40.0, S)
+    pl[rng.random(pl.shape) < 0.15] = -np.inf
+    pl[0, 0, 1, S // 3:] = -np.inf
+    pl[1, 0, :] = -np.inf
+    po[np.isneginf(pl)] = 0.0
+    po32, pl32 = po.astype(np.float32), pl.astype(np.float32)
+    import split_kv_paged_page_amd as sk
+    dt = sk.ATTN_BF16 if dtype == "bf16" else sk.ATTN_F32
+    strides = (Hkv * P * D, P * D, D)   # a [page][head][token][dim] pool the merge never reads
+    desc = sk.make_desc(batch=B, q_len=1, num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D, head_dim_v=D,
+                        page_size=P, max_pages_per_req=S * 64 // P, dtype=dt, causal=0, v_aliases_k=0,
+                        num_pages=1, k_strides=strides, v_strides=strides)
+    plan = sk.attn_decode_plan(desc, 64 * S, S, 0)
+    o_off, l_off, nbytes = sk.attn_decode_workspace_layout(plan, S)
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    ws[o_off // 4: o_off // 4 + po32.size] = torch.from_numpy(po32.ravel()).cuda()
+    ws[l_off // 4: l_off // 4 + pl32.size] = torch.from_numpy(pl32.ravel()).cuda()
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = torch.full((B, 1, Hq, D), float("nan"), dtype=tdt, device="cuda")
+    lse = torch.full((B, 1, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    say(f"stage2 random partials S={S} {dtype}")
+    sk.attn_decode_merge(plan, S, ws, out, lse)
+    torch.cuda.synchronize()
+    mo, ml = oracle.merge_reference(po32.astype(np.float64), pl32.astype(np.float64))
+    assert row_rel_err(out.to(torch.float64).cpu().numpy(), mo) <= (1e-2 if dtype == "bf16" else 1e-5)
+    assert lse_err(lse.double().cpu().numpy(), ml) <= 1e-5
 
 
 # ---- full sizes, policy split count (the launch configuration the benchmark times) ----
