@@ -162,6 +162,9 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   p.fd_splits = splitkv::make_fastdiv((uint32_t)S);
   p.fd_group = splitkv::make_fastdiv((uint32_t)(d.num_q_heads / d.num_kv_heads));
   p.rows_total = p.group * d.q_len;
+  // One request: its context is most likely the longest the plan was made
+  // for.  Batches mix lengths, and a wrong guess costs more than it saves.
+  p.guess_ctx = d.batch == 1 ? plan->max_context_len : 0;
   p.rows_per_wg = plan->rows_per_wg;
   p.head_tiles = plan->head_tiles;
   p.xcd_remap = plan->xcd_remap;

@@ -35,6 +35,7 @@ struct Stage1Params {
   // index (see fastdiv.h); split_align = 1 << align_shift.
   FastDiv fd_tiles, fd_kvh, fd_batch, fd_splits, fd_group;
   int32_t align_shift;
+  int32_t guess_ctx;      // > 0: likely context length of every request (early page-table reads)
 };
 
 struct Stage2Params {

@@ -163,9 +163,53 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
                               p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch);
   const int tile = wc.tile, kvh = wc.kvh, b = wc.b, s = wc.s;
 
+  // The workgroup's last query row (rows differ in visible length only with
+  // causal drafts; every row of a workgroup belongs to one request).
+  const int first_row = tile * RW * 16;
+  int last_row = first_row + RW * 16 - 1;
+  if (last_row >= p.rows_total) last_row = p.rows_total - 1;
+  // Split bounds [sb_, se_) for context length Lc, and the workgroup's last
+  // visible key in the split (emax_, at least sb_).
+  auto bounds = [&](int Lc, int& sb_, int& se_, int& emax_) {
+    split_range(Lc, p.num_splits, p.fd_splits, p.align_shift, s, sb_, se_);
+    const int j = (int)fdiv((uint32_t)last_row, p.fd_group);
+    const int nv = p.causal ? Lc - p.q_len + 1 + j : Lc;
+    emax_ = nv < se_ ? nv : se_;
+    if (emax_ < sb_) emax_ = sb_;
+  };
+
+  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
+  const int psh = p.page_shift, P = p.page_size;
+
+  // Ring path: page ids travel through LDS.  Block X's ids are DMA'd into
+  // slot X % NB of this wave's ring (lane k: key k % 32).  A page id loaded
+  // into a register would make the compiler wait for every DMA in flight
+  // before its first use.
+  constexpr int NB = C::NBUF, D = NB - 1;
+  uint8_t* pid_ring = smem + C::TILES + wave * NB * 256;
+  auto issue_pid_at = [&](int sb_, int emax_, int blk_idx, int slot) {
+    const int t = sb_ + (kw + blk_idx * KW) * 32 + (lane & 31);
+    const int tc = t < emax_ ? t : emax_ - 1;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(pt + (tc >> psh)),
+                                     (__attribute__((address_space(3))) void*)(pid_ring + slot * 256), 4, 0, 0);
+  };
+  // With one request (p.guess_ctx > 0, the plan's longest context), the
+  // first blocks' ids are requested before the context length arrives, on
+  // the guess that the request has that length; a wrong guess costs a wait
+  // and a second request.  That takes one dependent load off the start.
+  int sb_g = 0, se_g = 0, em_g = 0;
+  if constexpr (NB > 1) {
+    if (p.guess_ctx > 0) bounds(p.guess_ctx, sb_g, se_g, em_g);
+    if (em_g > sb_g) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) issue_pid_at(sb_g, em_g, j, j);
+    }
+  }
+
   const int L = p.ctx[b];
-  int sb, se;
-  split_range(L, p.num_splits, p.fd_splits, p.align_shift, s, sb, se);
+  int sb, se, end_max;
+  bounds(L, sb, se, end_max);
+  const bool guess_ok = em_g > sb_g && sb_g == sb && em_g == end_max;
 
   // This lane's query row and its visible end.
   const int gr = (tile * RW + rw) * 16 + n;
@@ -177,21 +221,7 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
     row_end = nv < se ? nv : se;
     if (row_end < sb) row_end = sb;
   }
-  // The workgroup's last visible key over all its rows (rows differ only with
-  // causal drafts; every row of a workgroup belongs to one request).
-  const int first_row = tile * RW * 16;
-  int last_row = first_row + RW * 16 - 1;
-  if (last_row >= p.rows_total) last_row = p.rows_total - 1;
-  int end_max = sb;
-  {
-    const int j = (int)fdiv((uint32_t)last_row, p.fd_group);
-    const int nv = p.causal ? L - p.q_len + 1 + j : L;
-    end_max = nv < se ? nv : se;
-    if (end_max < sb) end_max = sb;
-  }
 
-  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
-  const int psh = p.page_shift, P = p.page_size;
   // Stream kw takes blocks it = 0, 1, ... at keys sb + (kw + it*KW)*32.  All
   // streams run the same trip count so shared-tile barriers stay uniform.
   const int nit = (end_max - sb + 32 * KW - 1) / (32 * KW);
@@ -429,30 +459,24 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
     // the explicit wait for block it counts exactly the loads issued after
     // it: D - 1 x (one page-id load + this wave's DMAs).  Near the end of the
     // split fewer blocks follow, and the wait is for everything.
-    constexpr int NB = C::NBUF, D = NB - 1;
-    // Page ids travel through LDS as well: block X's ids are DMA'd into slot
-    // X % NB of this wave's ring (lane k: key k % 32) just before block X - D
-    // is issued, so the wait for block X - D covers them.  A page id loaded
-    // into a register would make the compiler wait for every DMA in flight
-    // before its first use.
-    uint8_t* pid_ring = smem + C::TILES + wave * NB * 256;
+    // Block X's ids are requested just before block X - D is issued, so the
+    // wait for block X - D covers them.
     const uint32_t pid_addr = lds_addr(pid_ring) + dkey0 * 4;   // entry k: key k % 32
-    auto issue_pid = [&](int blk_idx, int slot) {
-      const int t = blk_of(blk_idx) + (lane & 31);
-      const int tc = t < end_max ? t : end_max - 1;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(pt + (tc >> psh)),
-                                       (__attribute__((address_space(3))) void*)(pid_ring + slot * 256), 4, 0, 0);
-    };
+    auto issue_pid = [&](int blk_idx, int slot) { issue_pid_at(sb, end_max, blk_idx, slot); };
     // This lane's two DMA keys' page ids from ring slot `slot` (the caller
     // waits for them with lds_wait2).
     auto read_pids = [&](int slot, int& p0, int& p1) {
       p0 = lds_read_b32<0>(pid_addr + slot * 256);
       p1 = lds_read_b32<64>(pid_addr + slot * 256);
     };
-    // Prologue: ids of blocks 0 .. D-1, then blocks 0 .. D-1 themselves
-    // (each preceded by the ids of block j + D).
+    // Prologue: ids of blocks 0 .. D-1 (unless the guess above already asked
+    // for them; a wrong guess's loads land before the second request), then
+    // blocks 0 .. D-1 themselves (each preceded by the ids of block j + D).
+    if (!guess_ok) {
+      wait_vmcnt<0>();
 #pragma unroll
-    for (int j = 0; j < D; ++j) issue_pid(j, j);
+      for (int j = 0; j < D; ++j) issue_pid(j, j);
+    }
     wait_vmcnt<0>();
 #pragma unroll
     for (int j = 0; j < D; ++j) {
@@ -485,6 +509,9 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
       return it % NB;
     });
   }
+  // No direct-to-LDS load (the trailing page-id requests, an unused guess)
+  // may still be in flight when the wave's LDS is released.
+  if constexpr (C::NBUF > 1) wait_vmcnt<0>();
 
   l = sum_xor32(sum_xor16(l));
   auto write_row = [&](int grr, int d, float4 o, float lse) {

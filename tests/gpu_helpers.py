@@ -34,7 +34,7 @@ def validate_inputs(inp):
 class Decode:
     """One uploaded problem + plan; run() calls attn_decode_run."""
 
-    def __init__(self, inp, num_splits=0, flags=0, max_splits=None):
+    def __init__(self, inp, num_splits=0, flags=0, max_splits=None, max_context_len=None):
         import torch
         validate_inputs(inp)
         self.inp = inp
@@ -44,6 +44,8 @@ class Decode:
         self.desc = sk.make_desc_from_tensors(t["q"], t["k_cache"], t["v_cache"], t["page_table"],
                                               head_dim_v=w.head_dim_v, causal=w.causal)
         mx = int(max(inp.context_lens)) if len(inp.context_lens) else 0
+        if max_context_len is not None:
+            mx = max_context_len
         self.plan = sk.attn_decode_plan(self.desc, mx, max_splits or num_splits, flags)
         self.S = num_splits or self.plan.num_splits
         self.dtype = torch.float32 if w.kv_dtype == "f32" else torch.bfloat16

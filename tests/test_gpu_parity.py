@@ -123,6 +123,29 @@ def test_parity_forced_splits(name, splits):
         check_against_oracle(d, tol_for(w), S=S)
 
 
+@pytest.mark.parametrize("name,extra", [("gqa_64k_s5000", (0, 1, 63, 64, 3000)),
+                                        ("drafts_b1", (0, 1, 700)),
+                                        ("mla_wide_b1", (0, 65))])
+def test_plan_sized_for_longer_contexts(name, extra):
+    """A single request whose context is shorter than the plan's longest:
+    the kernels guess the plan's length for their first page-table reads
+    and must recover when the guess is wrong (and use it when right)."""
+    cases = dict(small_cases(), drafts_b1=scaled("varlen_drafts", context_lens=(1500,), seed=26),
+                 mla_wide_b1=scaled("mla_wide", context_lens=(2049,), seed=27))
+    w = cases[name]
+    inp = inputs(name, w)
+    L = int(inp.context_lens[0])
+    # a page table wide enough for the longest plan (extra entries: page 0)
+    cols = -(-(L + max(extra)) // w.page_size)
+    pt = np.zeros((1, cols), dtype=np.int32)
+    pt[:, :inp.page_table.shape[1]] = inp.page_table
+    inp = inp.with_(page_table=pt)
+    for e in extra:
+        say(f"longer plan {name} ctx={L} plan max={L + e}")
+        d = Decode(inp, max_context_len=L + e).run()
+        check_against_oracle(d, tol_for(w))
+
+
 def test_empty_contexts_and_splits():
     w = scaled("gqa_64k", context_lens=(0, 5, 64, 65, 0, 130), pool_pages=64, seed=9)
     inp = generate(w)
