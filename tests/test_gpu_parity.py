@@ -312,22 +312,24 @@ def test_stage2_alone_on_oracle_partials(name, S):
     assert lse_err(d.lse_f64(), ml) <= 1e-5
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("S", [2, 16, 17, 256, 257, 700])
-def test_stage2_alone_on_random_partials(S, dtype):
+@pytest.mark.parametrize("S,Hq,dtype", [(S, Hq, "bf16") for S in (2, 16, 17, 256, 257, 700) for Hq in (2, 4, 16)] +
+                         [(S, 16, "f32") for S in (16, 17, 700)])
+def test_stage2_alone_on_random_partials(S, Hq, dtype):
     """The merge on seeded partials of every kind the split rule can leave:
     split log-sum-exps spread over +-20 (up to 80 apart within one row),
-    empty splits (-inf) scattered and in runs, one row with every split
-    empty.  Split counts on both sides of the two kernels' boundary (16)
-    and of the register chunk of the many-split kernel (256)."""
-    B, Hq, Hkv, D, P = 2, 16, 2, 128, 16
+    empty splits (-inf) scattered and in runs, half of one request's rows
+    with every split empty.  Split counts on both sides of the two kernels' boundary (16)
+    and of the register chunk of the many-split kernel (256); 2, 4 and 16
+    query heads (two requests) give the many-split kernel 64, 32 and 16
+    lanes per output."""
+    B, Hkv, D, P = 2, 2, 128, 16
     rng = np.random.default_rng(1000 + S)
     po = rng.standard_normal((B, 1, Hq, S, D))
     pl = rng.uniform(-20.0, 20.0, (B, 1, Hq, S))
     pl[0, 0, 0] += np.linspace(0.0, 40.0, S)
     pl[rng.random(pl.shape) < 0.15] = -np.inf
     pl[0, 0, 1, S // 3:] = -np.inf
-    pl[1, 0, :] = -np.inf
+    pl[B - 1, 0, Hq // 2:] = -np.inf
     po[np.isneginf(pl)] = 0.0
     po32, pl32 = po.astype(np.float32), pl.astype(np.float32)
     import split_kv_paged_page_amd as sk
