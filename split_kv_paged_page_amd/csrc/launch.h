@@ -63,6 +63,8 @@ hipError_t launch_stage1_mfma(const Stage1Params& p, int dk, int dv, bool v_alia
                               hipStream_t s);
 
 bool stage2_supported(int dtype, int dv);
+// Lanes per output pair (query row, 4 dims) the merge uses.
+int stage2_lanes(int64_t pairs, int num_splits);
 hipError_t launch_stage2(const Stage2Params& p, int dtype, hipStream_t s);
 
 }  // namespace splitkv
