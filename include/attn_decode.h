@@ -82,10 +82,9 @@ enum {
 
 /* Kernel families the planner picks from. */
 enum {
-  ATTN_VARIANT_VALU = 1,            /* vector-ALU stage 1 (fp32; bf16 with fewer than 8 rows
-                                       per KV head or head dims without a matrix-core kernel) */
-  ATTN_VARIANT_MFMA = 2             /* matrix-core stage 1 (bf16, 8 or more rows per KV head,
-                                       head dims 128/128, 256/256 or 576/512 with V = K[:512]) */
+  ATTN_VARIANT_VALU = 1,            /* vector-ALU stage 1 (fp32: head dims 64/64, 128/128) */
+  ATTN_VARIANT_MFMA = 2             /* matrix-core stage 1 (bf16: head dims 128/128, 256/256,
+                                       576/512 with V = K[:512]) */
 };
 
 /* Shape and layout of one decode call; filled by the caller. */

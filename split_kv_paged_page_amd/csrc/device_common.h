@@ -98,21 +98,10 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return a + b;
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
-
 // fp32 -> bf16, nearest-even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2_t f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-__device__ __forceinline__ uint16_t to_bf16(float x) {
-  return (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
-}
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
-                                         c, false);
 }
 
 // 2^x; exact at 0, 0 for -inf.

@@ -27,6 +27,7 @@ attn_status hip_fail(hipError_t e, const char* what) {
 
 constexpr int kSplitAlign = 64;   // keys per stage-1 block and split granule
 constexpr int kNumCu = 256;       // MI355X compute units
+constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kMaxSplits = 4096;  // far above any useful split count; bounds the workspace
 
 uint64_t fnv1a(const void* p, size_t n, uint64_t h = 1469598103934665603ull) {
@@ -238,16 +239,17 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
   p.split_align = kSplitAlign;
   p.flags = flags;
   p.xcd_remap = (flags & ATTN_PLAN_NO_XCD_REMAP) ? 0 : 1;
-  // Matrix cores where 8 or more query rows share a KV head (bf16, head dims
-  // with a matrix-core kernel): a 16-row tile is then at least half full, and
-  // its Q.K and P.V cost a fraction of the vector-ALU work per key.  Fewer
-  // rows, fp32 and other head dims stay on the vector ALUs.
+  // bf16 runs on the matrix cores at every group size (a 16-row tile part
+  // empty still costs a fraction of the vector-ALU work per key); fp32 runs
+  // on the vector ALUs.
   const splitkv::MfmaShape ms =
       splitkv::stage1_mfma_shape(d.dtype, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0, rows);
+  int wgs_per_cu = 2;
   if (ms.rw > 0) {
     p.variant = ATTN_VARIANT_MFMA;
     p.rows_per_wg = 16 * ms.rw;
     p.stage1_waves = ms.rw * ms.kw;
+    wgs_per_cu = kLdsPerCu / ms.smem < 2 ? 1 : 2;
   } else {
     const int rt = pick_rows_per_wg(d.dtype, d.head_dim_qk, d.head_dim_v, rows);
     if (!rt)
@@ -272,11 +274,11 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
     S = kNumCu / d.batch;
     if (S < 1) S = 1;
   } else {
-    // VALU workgroups and lone MFMA waves (a 48 KB ring) fit two per CU;
-    // larger MFMA workgroups (144-148 KB of LDS tiles, or a full register
-    // file per wave) one per CU: aim for one full round.
+    // One full round of workgroups: two per CU where the LDS allows it (VALU
+    // workgroups, the lone MFMA wave at head dim 128), else one.  A third
+    // lone wave per CU was measured slower (64K GQA: 16.3 us against 15.7).
     const int per_split = d.batch * d.num_kv_heads * p.head_tiles;
-    const int target = p.variant == ATTN_VARIANT_MFMA && p.stage1_waves > 1 ? kNumCu : 2 * kNumCu;
+    const int target = wgs_per_cu * kNumCu;
     S = target / per_split;
     if (S > blocks) S = blocks;
     if (S < 1) S = 1;

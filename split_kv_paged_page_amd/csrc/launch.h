@@ -53,10 +53,10 @@ struct Stage2Params {
 bool stage1_valu_supported(int dtype, int dk, int dv, int rows_per_wg);
 hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, hipStream_t s);
 
-// Matrix-core workgroup shape: rw 16-row tiles x kw key streams ({0, 0}: no
-// matrix-core kernel for this dtype, head dims and rows per KV head).
+// Matrix-core workgroup shape: rw 16-row tiles x kw key streams and its LDS
+// bytes ({0, 0, 0}: no matrix-core kernel for this dtype and head dims).
 struct MfmaShape {
-  int rw, kw;
+  int rw, kw, smem;
 };
 MfmaShape stage1_mfma_shape(int dtype, int dk, int dv, bool v_aliases_k, int rows);
 hipError_t launch_stage1_mfma(const Stage1Params& p, int dk, int dv, bool v_aliases_k, MfmaShape shape,

@@ -1,10 +1,11 @@
-// Stage 1 of split-KV paged decode on the matrix cores (gfx950), for KV heads
-// shared by 8 or more query rows: an MLA latent head (aiter PR #4758,
-// "[Gluon][MLA] Deeper async-copy pipeline in the bh16 stage-1 decode loop",
-// bh16 / bh64 regimes), a GQA group, or a wide GQA group with draft tokens.
+// Stage 1 of split-KV paged decode on the matrix cores (gfx950), for bf16 KV
+// caches: an MLA latent head (aiter PR #4758, "[Gluon][MLA] Deeper
+// async-copy pipeline in the bh16 stage-1 decode loop", bh16 / bh64
+// regimes), a GQA group, or a wide GQA group with draft tokens.
 //
-// Each wave owns 16 query rows (a group of 8 fills half of the tile; the
-// matrix cores have throughput to spare at decode's few flops per byte).  A
+// Each wave owns 16 query rows; smaller groups leave part of the tile empty
+// (decode does so few flops per byte that the matrix cores idle either way,
+// and one 16x16x32 MFMA still replaces hundreds of vector-ALU issues).  A
 // workgroup has RW x KW waves: RW 16-row tiles that share each K/V block
 // through a ring of LDS tiles (one barrier per block), or KW key streams that
 // take the split's 32-key blocks in turn with their own tile and running max
@@ -12,8 +13,9 @@
 //   * 64+ (wide MLA), 32 (draft groups): 4 or 2 tiles on a ring of 4 (three
 //     blocks in flight), each block read once per 64 or 32 rows;
 //   * 16 (MLA bh16): one tile, four key streams, load -> wait -> compute;
-//   * 8-15 (GQA): one wave alone on a ring of 3 (two blocks in flight),
-//     48 KB of LDS at head dim 128, two or three workgroups per CU.
+//   * 1-15 (GQA, MLA with few heads): one wave alone on a ring of 3 (two
+//     blocks in flight); 48 KB of LDS at head dim 128 (two workgroups per
+//     CU), 97 KB at 256 and 109 KB at 576 (one).
 // Per block:
 //   * page walk: lane k < 32 looks up key k's page; keys past the visible end
 //     clamp to the last visible key (weight 0 later);
@@ -593,26 +595,36 @@ struct Entry {
   int rw, kw;
   int min_rows;   // rows per KV head this shape needs
   void (*fn)(Stage1Params);
+  int smem;       // LDS bytes per workgroup
 };
+
+template <int DK, int DV, bool VALIAS, int RW, int KW>
+constexpr Entry mk(int min_rows) {
+  return {DK, DV, VALIAS, RW, KW, min_rows, &stage1_mfma_kernel<DK, DV, VALIAS, RW, KW>,
+          MCfg<DK, DV, VALIAS, RW, KW>::SMEM};
+}
 
 // Per head-dim pair, in order of preference: the first entry whose min_rows
 // the group reaches is used.
 constexpr Entry kTable[] = {
-    {576, 512, true, 4, 1, 64, &stage1_mfma_kernel<576, 512, true, 4, 1>},
-    {576, 512, true, 1, 4, 16, &stage1_mfma_kernel<576, 512, true, 1, 4>},
-    {256, 256, false, 2, 1, 32, &stage1_mfma_kernel<256, 256, false, 2, 1>},
-    {256, 256, false, 1, 4, 16, &stage1_mfma_kernel<256, 256, false, 1, 4>},
-    {128, 128, false, 1, 4, 16, &stage1_mfma_kernel<128, 128, false, 1, 4>},
-    {128, 128, false, 1, 1, 8, &stage1_mfma_kernel<128, 128, false, 1, 1>},
+    mk<576, 512, true, 4, 1>(64),
+    mk<576, 512, true, 1, 4>(16),
+    mk<576, 512, true, 1, 1>(1),
+    mk<256, 256, false, 2, 1>(32),
+    mk<256, 256, false, 1, 4>(16),
+    mk<256, 256, false, 1, 1>(1),
+    mk<128, 128, false, 1, 4>(16),
+    mk<128, 128, false, 1, 1>(1),
 };
 
 }  // namespace
 
 MfmaShape stage1_mfma_shape(int dtype, int dk, int dv, bool v_aliases_k, int rows) {
-  if (dtype != 1) return MfmaShape{0, 0};
+  if (dtype != 1) return MfmaShape{0, 0, 0};
   for (const Entry& e : kTable)
-    if (e.dk == dk && e.dv == dv && e.valias == v_aliases_k && rows >= e.min_rows) return MfmaShape{e.rw, e.kw};
-  return MfmaShape{0, 0};
+    if (e.dk == dk && e.dv == dv && e.valias == v_aliases_k && rows >= e.min_rows)
+      return MfmaShape{e.rw, e.kw, e.smem};
+  return MfmaShape{0, 0, 0};
 }
 
 hipError_t launch_stage1_mfma(const Stage1Params& p, int dk, int dv, bool v_aliases_k, MfmaShape sh,

@@ -1,11 +1,10 @@
-// Stage 1 of split-KV paged decode on the vector ALUs (gfx950, wave64).
+// Stage 1 of split-KV paged decode on the vector ALUs (gfx950, wave64), for
+// fp32 KV caches (bf16 caches run on the matrix cores, at every group size).
 //
 // One workgroup scores one split of one request's keys against RT query rows
 // that share a KV head (aiter PR #4758, "[Gluon][MLA] Deeper async-copy
 // pipeline in the bh16 stage-1 decode loop", Motivation: each stage-1
-// program walks its split's KV blocks).  It serves fp32 caches, and bf16
-// groups of fewer than 8 rows per KV head (or head dims without a
-// matrix-core kernel), where a 16-row matrix-core tile would be mostly empty.
+// program walks its split's KV blocks).
 //
 // NW waves take 64-key blocks of the split in turn, each with its own
 // running max / sum / accumulator, merged at the end.  Per wave and block:
@@ -21,16 +20,14 @@
 //     several rows contiguously; the pad goes between load groups, as
 //     rocm-libraries PR #10102 does for its head-dim-64 K tile (Motivation
 //     bank table, Technical Details);
-//   * Q.K: lane t owns key t and forms all RT dot products; the query rows are
-//     wave-uniform and sit in SGPRs (scalar loads), the scalar operand of
-//     v_dot2 / v_fma, so they cost no LDS bandwidth;
+//   * Q.K: lane t owns key t and forms all RT dot products with FMAs; the
+//     workgroup's query rows sit in LDS and each 16-byte chunk is one
+//     broadcast read serving all 64 keys;
 //   * softmax: each 16-lane DPP row keeps its own running max per query row;
 //   * P.V: the 16 lanes of DPP row g accumulate keys 16g..16g+15; lane x owns
 //     a contiguous slice of the head dim, so V rows arrive as coalesced
 //     256-byte (or wider) segments, and key i's weight reaches the row's
-//     lanes through row_newbcast:i.  For bf16 the weights of a key pair are
-//     rounded to one bf16x2 and both keys go through one v_dot2_f32_bf16 per
-//     output element (fp32 accumulation); fp32 inputs keep fp32 weights.
+//     lanes through row_newbcast:i.
 #include <utility>
 
 #include "device_common.h"
@@ -42,9 +39,9 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 
-template <int DTYPE, int DK, int DV, int RT, int NW>
+template <int DK, int DV, int RT, int NW>
 struct Cfg {
-  static constexpr int ES = DTYPE == 0 ? 4 : 2;  // element bytes
+  static constexpr int ES = 4;                   // element bytes (fp32)
   static constexpr int KRB = DK * ES;            // bytes of one K row
   static constexpr int VRB = DV * ES;            // bytes of one V row
   static constexpr int KCH = KRB / 16;           // 16-byte chunks of a K row
@@ -60,12 +57,13 @@ struct Cfg {
   static constexpr int QB = RT * KRB;            // the workgroup's query rows
   static constexpr int SMEM = NW * WAVE_B + QB;
   static_assert(VRB % 256 == 0 && KRB % 16 == 0, "row sizes");
+  static_assert(KLDS, "K rows of 16 to 64 chunks go through the LDS tile");
   static_assert(RT * VE <= 128, "accumulator budget");
 };
 
-template <int DTYPE, int DK, int DV, int RT, int NW>
+template <int DK, int DV, int RT, int NW>
 __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
-  using C = Cfg<DTYPE, DK, DV, RT, NW>;
+  using C = Cfg<DK, DV, RT, NW>;
   constexpr int ES = C::ES, KRB = C::KRB, KCH = C::KCH, VU4 = C::VU4, VE = C::VE;
 
   __shared__ __align__(16) uint8_t smem[C::SMEM];
@@ -158,7 +156,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
     if (blk + NW * 64 < end_max) page_next = page_of(blk + NW * 64);
 
     // ---- issue K (straight into the LDS tile), then V (16 rows per DPP row) ----
-    if constexpr (C::KLDS && C::RPI == 4) {
+    if constexpr (C::RPI == 4) {
       // Load i moves keys i, 16+i, 32+i, 48+i (one per DPP row); each row
       // takes its key's offset by row_newbcast, no LDS round trip.
       [&]<int... I>(std::integer_sequence<int, I...>) {
@@ -169,7 +167,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
         };
         (one(std::integral_constant<int, I>{}), ...);
       }(std::make_integer_sequence<int, 16>{});
-    } else if constexpr (C::KLDS) {
+    } else {
       // Load i moves keys i*RPI .. i*RPI + RPI - 1 (offsets by ds_bpermute).
       uint32_t offs[C::KINS];
 #pragma unroll
@@ -204,20 +202,13 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         const uint4 qc = *(const uint4*)(q_lds + qoff + r * KRB + c * 16);
-        if constexpr (DTYPE == 0) {
-          sc[r] = fmaf(__builtin_bit_cast(float, qc.x), __builtin_bit_cast(float, kc.x), sc[r]);
-          sc[r] = fmaf(__builtin_bit_cast(float, qc.y), __builtin_bit_cast(float, kc.y), sc[r]);
-          sc[r] = fmaf(__builtin_bit_cast(float, qc.z), __builtin_bit_cast(float, kc.z), sc[r]);
-          sc[r] = fmaf(__builtin_bit_cast(float, qc.w), __builtin_bit_cast(float, kc.w), sc[r]);
-        } else {
-          sc[r] = dot2_bf16(qc.x, kc.x, sc[r]);
-          sc[r] = dot2_bf16(qc.y, kc.y, sc[r]);
-          sc[r] = dot2_bf16(qc.z, kc.z, sc[r]);
-          sc[r] = dot2_bf16(qc.w, kc.w, sc[r]);
-        }
+        sc[r] = fmaf(__builtin_bit_cast(float, qc.x), __builtin_bit_cast(float, kc.x), sc[r]);
+        sc[r] = fmaf(__builtin_bit_cast(float, qc.y), __builtin_bit_cast(float, kc.y), sc[r]);
+        sc[r] = fmaf(__builtin_bit_cast(float, qc.z), __builtin_bit_cast(float, kc.z), sc[r]);
+        sc[r] = fmaf(__builtin_bit_cast(float, qc.w), __builtin_bit_cast(float, kc.w), sc[r]);
       }
     };
-    if constexpr (C::KLDS) {
+    {
       // K has landed once at most the V loads are outstanding.
       wait_vmcnt<16 * VU4>();
       // Where key `lane` sits in the tile (see the two load orders above).
@@ -226,10 +217,6 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
 #pragma unroll 2
       for (int c = 0; c < KCH; ++c) dot_chunk(*(const uint4*)(krow + c * 16), c);
       __builtin_amdgcn_wave_barrier();
-    } else {
-      const uint8_t* krow = kbase + (uint64_t)koff * 16;
-#pragma unroll 8
-      for (int c = 0; c < KCH; ++c) dot_chunk(*(const uint4*)(krow + c * 16), c);
     }
 
     // ---- online softmax, per 16-lane row ----
@@ -254,8 +241,8 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
       }
     }
 
-    if constexpr (DTYPE == 0) {
-      // fp32: P.V with fp32 weights and FMAs.
+    {
+      // P.V with fp32 weights and FMAs.
 #pragma unroll
       for (int r = 0; r < RT; ++r) l[r] += pr[r];
       [&]<int... I>(std::integer_sequence<int, I...>) {
@@ -276,45 +263,6 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
         };
         (one(std::integral_constant<int, I>{}), ...);
       }(std::make_integer_sequence<int, 16>{});
-    } else {
-      // bf16: weights of keys 2i and 2i+1 travel as one bf16 pair, V of the
-      // two keys is interleaved by v_perm, and v_dot2_f32_bf16 accumulates
-      // both keys in fp32.  The row sum keeps the fp32 weights: the
-      // log-sum-exp must hold to 1e-3, which bf16 weights (2^-9 relative
-      // each) cannot promise for short splits.
-      const bool odd = x & 1;
-      uint32_t pp[RT];
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const float other = dpp_f32<kDppQuadSwap1>(pr[r]);
-        pp[r] = pack_bf16x2(odd ? other : pr[r], odd ? pr[r] : other);
-        l[r] += pr[r];
-      }
-      [&]<int... I>(std::integer_sequence<int, I...>) {
-        auto pair = [&](auto ic) {
-          constexpr int i = decltype(ic)::value;  // keys 2i, 2i+1 of the row
-          uint32_t pw[RT];
-#pragma unroll
-          for (int r = 0; r < RT; ++r) pw[r] = (uint32_t)row_bcast_i32<2 * i>((int)pp[r]);
-#pragma unroll
-          for (int u = 0; u < VU4; ++u) {
-            const uint32_t a[4] = {vv[2 * i][u].x, vv[2 * i][u].y, vv[2 * i][u].z, vv[2 * i][u].w};
-            const uint32_t c[4] = {vv[2 * i + 1][u].x, vv[2 * i + 1][u].y, vv[2 * i + 1][u].z,
-                                   vv[2 * i + 1][u].w};
-#pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) {
-              const uint32_t lo = __builtin_amdgcn_perm(c[w2], a[w2], 0x05040100u);  // dim 2w2
-              const uint32_t hi = __builtin_amdgcn_perm(c[w2], a[w2], 0x07060302u);  // dim 2w2+1
-#pragma unroll
-              for (int r = 0; r < RT; ++r) {
-                acc[r][u * 8 + 2 * w2] = dot2_bf16(pw[r], lo, acc[r][u * 8 + 2 * w2]);
-                acc[r][u * 8 + 2 * w2 + 1] = dot2_bf16(pw[r], hi, acc[r][u * 8 + 2 * w2 + 1]);
-              }
-            }
-          }
-        };
-        (pair(std::integral_constant<int, I>{}), ...);
-      }(std::make_integer_sequence<int, 8>{});
     }
   }
 
@@ -372,7 +320,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
     const int j = (int)fdiv((uint32_t)gr, p.fd_group), h = kvh * p.group + gr - j * p.group;
     const int64_t row = ((int64_t)b * p.q_len + j) * p.num_q_heads + h;
     if (p.out) {
-      store_out4(p.out, DTYPE, row * DV + d, o);
+      store_out4(p.out, 0, row * DV + d, o);
       if (d == 0 && p.lse_out) p.lse_out[row] = lse;
     } else {
       *(float4*)(p.o_part + (row * p.num_splits + s) * DV + d) = o;
@@ -382,25 +330,24 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
 }
 
 struct Entry {
-  int dtype, dk, dv, rt, nw;
+  int dk, dv, rt, nw;
   void (*fn)(Stage1Params);
 };
 
-template <int DTYPE, int DK, int DV, int RT, int NW = 4>
+template <int DK, int DV, int RT, int NW = 4>
 constexpr Entry entry() {
-  return {DTYPE, DK, DV, RT, NW, &stage1_valu_kernel<DTYPE, DK, DV, RT, NW>};
+  return {DK, DV, RT, NW, &stage1_valu_kernel<DK, DV, RT, NW>};
 }
 
 constexpr Entry kTable[] = {
-    entry<0, 64, 64, 4>(),   entry<0, 64, 64, 8>(),   entry<0, 64, 64, 16>(),
-    entry<0, 128, 128, 4>(), entry<0, 128, 128, 8>(), entry<0, 128, 128, 16>(),
-    entry<1, 128, 128, 4>(), entry<1, 128, 128, 8>(),
-    entry<1, 256, 256, 4>(), entry<1, 256, 256, 8>(), entry<1, 576, 512, 4>(),
+    entry<64, 64, 4>(),  entry<64, 64, 8>(),  entry<64, 64, 16>(),
+    entry<128, 128, 4>(), entry<128, 128, 8>(), entry<128, 128, 16>(),
 };
 
 const Entry* find(int dtype, int dk, int dv, int rt) {
+  if (dtype != 0) return nullptr;   // fp32 only
   for (const Entry& e : kTable)
-    if (e.dtype == dtype && e.dk == dk && e.dv == dv && e.rt == rt) return &e;
+    if (e.dk == dk && e.dv == dv && e.rt == rt) return &e;
   return nullptr;
 }
 

@@ -107,23 +107,41 @@ def test_default_policy_fills_the_chip():
 def test_kernel_choice_by_rows_per_kv_head():
     # (query heads, KV heads, q_len, head dims, dtype) -> (variant, rows per workgroup, waves)
     V, M = sk.ATTN_VARIANT_VALU, sk.ATTN_VARIANT_MFMA
+    F32 = sk.ATTN_F32
     cases = [
-        (dict(Hq=8), (V, 4, 4)),                          # 4 rows: vector ALUs
-        (dict(Hq=12), (V, 8, 4)),                         # 6 rows
-        (dict(Hq=16), (M, 16, 1)),                        # 8 rows: one wave on a ring, half a tile
+        (dict(Hq=2), (M, 16, 1)),                         # 1 row: one wave on a ring, tile mostly empty
+        (dict(Hq=8), (M, 16, 1)),                         # 4 rows
+        (dict(Hq=16), (M, 16, 1)),                        # 8 rows
         (dict(Hq=24), (M, 16, 1)),                        # 12 rows
         (dict(Hq=32), (M, 16, 4)),                        # 16 rows: four key streams
-        (dict(Hq=16, dtype=sk.ATTN_F32), (V, 8, 4)),      # fp32 stays on the vector ALUs
+        (dict(Hq=40), (M, 16, 4)),                        # 20 rows: two head tiles
         (dict(Hq=64, Hkv=8, q_len=4, Dk=256, Dv=256, causal=1), (M, 32, 2)),   # 32 draft rows
-        (dict(Hq=16, Hkv=2, Dk=256, Dv=256), (V, 8, 4)),  # 8 rows at head dim 256
+        (dict(Hq=16, Hkv=2, Dk=256, Dv=256), (M, 16, 1)), # 8 rows at head dim 256
+        (dict(Hq=8, dtype=F32), (V, 4, 4)),               # fp32 stays on the vector ALUs
+        (dict(Hq=16, dtype=F32), (V, 8, 4)),
+        (dict(Hq=32, dtype=F32), (V, 16, 4)),
+        (dict(Hq=4, Hkv=1, Dk=64, Dv=64, dtype=F32), (V, 4, 4)),
     ]
     for kw, want in cases:
         p = sk.attn_decode_plan(desc(**kw), 4096, 0)
         assert (p.variant, p.rows_per_wg, p.stage1_waves) == want, (kw, want)
-    p = sk.attn_decode_plan(mla_desc(48), 68000, 0)
-    assert (p.variant, p.rows_per_wg, p.stage1_waves) == (M, 16, 4)
-    p = sk.attn_decode_plan(desc(Hq=128, Hkv=1, Dk=576, Dv=512, P=1, maxp=68000, alias=1, pages=655360), 68000, 0)
-    assert (p.variant, p.rows_per_wg, p.stage1_waves) == (M, 64, 4)
+    mla = dict(Hkv=1, Dk=576, Dv=512, P=1, maxp=68000, alias=1, pages=655360)
+    for hq, want in ((4, (M, 16, 1)), (16, (M, 16, 4)), (128, (M, 64, 4))):
+        p = sk.attn_decode_plan(desc(Hq=hq, **mla), 68000, 0)
+        assert (p.variant, p.rows_per_wg, p.stage1_waves) == want, (hq, want)
+    with pytest.raises(sk.AttnDecodeError):      # no bf16 kernel at head dim 64
+        sk.attn_decode_plan(desc(Hq=4, Hkv=1, Dk=64, Dv=64), 4096, 0)
+
+
+def test_default_split_count_fills_one_round():
+    # two workgroups per CU where the LDS allows (vector-ALU kernel, the lone
+    # matrix-core wave at head dim 128), one otherwise
+    assert sk.attn_decode_plan(desc(), 65536, 0).num_splits == 512 // 2
+    assert sk.attn_decode_plan(desc(dtype=sk.ATTN_F32), 65536, 0).num_splits == 512 // 2
+    mla = dict(Hkv=1, Dk=576, Dv=512, P=1, maxp=68000, alias=1, pages=655360)
+    assert sk.attn_decode_plan(desc(B=48, Hq=4, **mla), 68000, 0).num_splits == 256 // 48
+    assert sk.attn_decode_plan(desc(B=48, Hq=16, **mla), 68000, 0).num_splits == 256 // 48
+    assert sk.attn_decode_plan(desc(B=6, Hq=32, Hkv=4, Dk=256, Dv=256), 2048, 0).num_splits == 256 // 24
 
 
 def test_plan_key_covers_shape_fields():
