@@ -83,8 +83,8 @@ enum {
 /* Kernel families the planner picks from. */
 enum {
   ATTN_VARIANT_VALU = 1,            /* vector-ALU stage 1 (fp32: head dims 64/64, 128/128) */
-  ATTN_VARIANT_MFMA = 2             /* matrix-core stage 1 (bf16: head dims 128/128, 256/256,
-                                       576/512 with V = K[:512]) */
+  ATTN_VARIANT_MFMA = 2             /* matrix-core stage 1 (bf16: head dims 64/64, 128/128,
+                                       256/256, 576/512 with V = K[:512]) */
 };
 
 /* Shape and layout of one decode call; filled by the caller. */

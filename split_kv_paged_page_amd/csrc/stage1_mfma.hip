@@ -14,8 +14,13 @@
 //     blocks in flight), each block read once per 64 or 32 rows;
 //   * 16 (MLA bh16): one tile, four key streams, load -> wait -> compute;
 //   * 1-15 (GQA, MLA with few heads): one wave alone on a ring of 3 (two
-//     blocks in flight); 48 KB of LDS at head dim 128 (two workgroups per
-//     CU), 97 KB at 256 and 109 KB at 576 (one).
+//     blocks in flight); 25 KB of LDS at head dim 64 and 49 KB at 128 (two
+//     workgroups per CU), 97 KB at 256 and 109 KB at 576 (one).
+// Head dims 64, 128, 256 and 576/512 share one tile layout (below).  At 64,
+// rocm-libraries PR #10102 pads groups of 128-byte K rows in LDS to spread
+// its reads over the banks (Motivation bank table); the XOR swizzle here
+// does that job without padding, for both the row reads of Q.K and the
+// transpose reads of P.V.
 // Per block:
 //   * page walk: lane k < 32 looks up key k's page; keys past the visible end
 //     clamp to the last visible key (weight 0 later);
@@ -634,6 +639,8 @@ constexpr Entry kTable[] = {
     mk<256, 256, false, 1, 1>(1),
     mk<128, 128, false, 1, 4>(16),
     mk<128, 128, false, 1, 1>(1),
+    mk<64, 64, false, 1, 4>(16),
+    mk<64, 64, false, 1, 1>(1),
 };
 
 }  // namespace

@@ -129,8 +129,9 @@ def test_kernel_choice_by_rows_per_kv_head():
     for hq, want in ((4, (M, 16, 1)), (16, (M, 16, 4)), (128, (M, 64, 4))):
         p = sk.attn_decode_plan(desc(Hq=hq, **mla), 68000, 0)
         assert (p.variant, p.rows_per_wg, p.stage1_waves) == want, (hq, want)
-    with pytest.raises(sk.AttnDecodeError):      # no bf16 kernel at head dim 64
-        sk.attn_decode_plan(desc(Hq=4, Hkv=1, Dk=64, Dv=64), 4096, 0)
+    assert sk.attn_decode_plan(desc(Hq=16, Dk=64, Dv=64), 4096, 0).variant == M     # bf16 head dim 64
+    with pytest.raises(sk.AttnDecodeError):      # no kernel at head dim 96
+        sk.attn_decode_plan(desc(Hq=16, Dk=96, Dv=96), 4096, 0)
 
 
 def test_default_split_count_fills_one_round():

@@ -41,6 +41,7 @@ def small_cases():
         "d256_g8": scaled("varlen_drafts", context_lens=(700, 2049, 64), q_len=1, causal=False, seed=30),
         "mla_h4": scaled("mla_b48", context_lens=(3000, 1, 2100), num_q_heads=4, prefix_len=0, prefix_group=0,
                          seed=29),
+        "gqa_d64_bf16": scaled("gqa_64k_d64", context_lens=(4100, 1, 700), seed=32),
         # fp32 runs on the vector ALUs: 8 and 16 rows at head dim 128
         "gqa_f32_g8": scaled("gqa_64k", context_lens=(3000, 1, 777), kv_dtype="f32", seed=28),
         "gqa_f32_g16": scaled("gqa_64k", context_lens=(2100, 300), num_q_heads=32, kv_dtype="f32", seed=31),
@@ -99,7 +100,7 @@ def test_parity_small(name):
 
 
 @pytest.mark.parametrize("name", ["gqa_64k_s5000", "mla_b4_private", "mla_wide_b4", "varlen_drafts",
-                                  "gqa_g4_bf16", "gqa_g12_bf16", "d256_g8", "mla_h4", "gqa_f32_g8"])
+                                  "gqa_g4_bf16", "gqa_g12_bf16", "d256_g8", "mla_h4", "gqa_f32_g8", "gqa_d64_bf16"])
 @pytest.mark.parametrize("top,q_gain", [(4.0, 1.0), (1.0, 8.0), (3.0, 4.0)])
 def test_parity_rising_and_peaked_scores(name, top, q_gain):
     # Keys scaled up along the context (and/or a peaked q) make the running
@@ -194,7 +195,7 @@ def designated_tokens(inp, S, where):
 
 
 @pytest.mark.parametrize("name", ["gqa_tiny_f32", "gqa_64k_b3_ragged", "mla_b48_b16", "mla_wide_b4",
-                                  "varlen_drafts", "mla_h4", "d256_g8", "gqa_f32_g16"])
+                                  "varlen_drafts", "mla_h4", "d256_g8", "gqa_f32_g16", "gqa_d64_bf16"])
 @pytest.mark.parametrize("where", ["first", "last"])
 def test_bitexact_gather_and_boundaries(name, where):
     """One-hot: the designated key of each split scores 2*dims above all
@@ -369,7 +370,7 @@ def test_stage2_alone_on_random_partials(S, Hq, dtype):
 
 # ---- full sizes, policy split count (the launch configuration the benchmark times) ----
 
-FULL = [("gqa_64k", None), ("varlen_drafts", None), ("mla_b48", (0, 13, 47)),
+FULL = [("gqa_64k", None), ("gqa_64k_d64", None), ("varlen_drafts", None), ("mla_b48", (0, 13, 47)),
         ("mla_wide", (0, 63)), ("mla_b48_ctl", (5, 40))]
 
 

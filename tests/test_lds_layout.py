@@ -124,7 +124,7 @@ def slot(k, c, s=swz):
     return (c >> 2) * 128 + 4 * k + ((c & 3) ^ s(k))
 
 
-@pytest.mark.parametrize("dk", [128, 256, 576])
+@pytest.mark.parametrize("dk", [64, 128, 256, 576])
 def test_mfma_tile_dma_fills_every_slot_once(dk):
     kch = dk * 2 // 16
     seen = {}
@@ -154,11 +154,12 @@ def pv_reads(dt, second_half, s=swz):
     return out
 
 
-def test_mfma_tile_reads_conflict_free():
-    for kk in range(18):
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (256, 256), (576, 512)])
+def test_mfma_tile_reads_conflict_free(dk, dv):
+    for kk in range(dk // 32):
         for h in (0, 1):
             assert max_phase_depth(qk_reads(kk, h), 16) == 1, (kk, h)
-    for dt in range(32):
+    for dt in range(dv // 16):
         for h in (0, 1):
             assert max_phase_depth(pv_reads(dt, h), 8) == 1, (dt, h)
 

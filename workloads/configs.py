@@ -1,6 +1,6 @@
 """Workload shapes for split-KV paged decode.
 
-Five workloads stand in for the traffic the pages measure:
+Six workloads stand in for the traffic the pages measure:
 
 * ``gqa_tiny_f32``   - tiny fp32 GQA decode (4 query heads over 1 KV head,
   head dim 64, 256 keys in 16 pages of 16, fixed 4 splits).
@@ -19,6 +19,9 @@ Five workloads stand in for the traffic the pages measure:
   32 query heads over 4 KV heads, head dim 256, page size 16.  The context
   lengths are the varlen sweep of rocm-libraries PR #10102 (Technical
   Details, launcher-cache paragraph).
+* ``gqa_64k_d64``    - the 64K GQA shape at head dim 64, bf16: the head dim
+  whose 128-byte K rows rocm-libraries PR #10102 pads in LDS (Motivation
+  bank table).
 
 The MLA batch-48 pool: six distinct 63,240-key prefixes plus 48 private
 4,760-key suffixes need 607,920 distinct slots, more than a 400k-token pool
@@ -124,6 +127,10 @@ def _mk() -> dict:
         name="varlen_drafts", batch=6, q_len=4, num_q_heads=32, num_kv_heads=4,
         head_dim_qk=256, head_dim_v=256, page_size=16, kv_dtype="bf16",
         context_lens=(256, 512, 768, 1024, 1536, 2048), pool_pages=768, causal=True, seed=5)
+    c["gqa_64k_d64"] = Workload(
+        name="gqa_64k_d64", batch=1, q_len=1, num_q_heads=16, num_kv_heads=2,
+        head_dim_qk=64, head_dim_v=64, page_size=16, kv_dtype="bf16",
+        context_lens=(65536,), pool_pages=8192, seed=6)
     return c
 
 
