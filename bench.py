@@ -26,6 +26,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# MI355X dense peaks: bf16 matrix cores (the bf16 kernel's Q.K and P.V), fp32
+# vector ALUs (the fp32 kernel).
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+VALU_F32_PEAK_TFLOPS = 157.3
 
 
 def parse():
@@ -49,14 +53,32 @@ def parse():
 def algorithmic_bytes(w, S):
     """Bytes one stage-1 launch must move at minimum: every visible key of
     every KV head once (V counted once when it aliases K), the page-table
-    entries, q, and the partial outputs + log-sum-exps it writes."""
+    entries, q, and the partial outputs + log-sum-exps it writes (with one
+    split: the output and log-sum-exp themselves)."""
     es = w.elem_bytes
     kv = w.logical_kv_bytes()
     pt = sum(-(-c // w.page_size) for c in w.context_lens) * 4
-    q = w.batch * w.q_len * w.num_q_heads * w.head_dim_qk * es
+    # q of the rows that see at least one key (causal rows before a short
+    # sequence's first token see none)
+    seen = sum(min(w.q_len, L) if w.causal else (w.q_len if L > 0 else 0) for L in w.context_lens)
+    q = seen * w.num_q_heads * w.head_dim_qk * es
     rows = w.batch * w.q_len * w.num_q_heads
-    part = rows * S * (w.head_dim_v + 1) * 4
+    part = rows * S * (w.head_dim_v + 1) * 4 if S > 1 else rows * (w.head_dim_v * es + 4)
     return kv, kv + pt + q + part
+
+
+def algorithmic_flops(w):
+    """2 x the multiply-adds the method needs: every query row against every
+    key it may see, over Dk for Q.K and Dv for P.V (causal rows see
+    max(0, L - q_len + 1 + j) keys)."""
+    pairs = 0
+    for L in w.context_lens:
+        if w.causal:
+            first = L - w.q_len + 1
+            pairs += sum(max(0, first + j) for j in range(w.q_len))
+        else:
+            pairs += w.q_len * L
+    return 2 * pairs * w.num_q_heads * (w.head_dim_qk + w.head_dim_v)
 
 
 def time_eager(fn_steps, steps, stream):
@@ -189,6 +211,10 @@ def main():
     us_s1 = ms1 * 1e3 / args.steps
     kv_gbs = kv_bytes / (us_op * 1e-6) / 1e9
     ach = alg_bytes / (us_s1 * 1e-6) / 1e9
+    flops = algorithmic_flops(w)
+    peak_tf = MFMA_BF16_PEAK_TFLOPS if w.kv_dtype == "bf16" else VALU_F32_PEAK_TFLOPS
+    # the kernel is bound by whichever of HBM and the compute units needs longer
+    compute_bound = flops / (peak_tf * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9)
 
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"stage1_traffic_{w.name}.json")
@@ -218,10 +244,16 @@ def main():
                    "num_splits": S, "rows_per_wg": plan.rows_per_wg, "head_tiles": plan.head_tiles,
                    "stage1_waves": plan.stage1_waves, "xcd_remap": plan.xcd_remap, "replicas": R,
                    "kv_bytes_per_op": kv_bytes, "parallelism": "single GPU"},
+        "tflops_per_s": round(flops / (us_op * 1e-6) / 1e12, 2),
         "roofline": {"bound": "hbm", "kernel": "stage1", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "alg_bytes_per_launch": alg_bytes, "launch_us": round(us_s1, 3)},
+                     "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": flops, "launch_us": round(us_s1, 3)},
     }
+    if compute_bound:
+        tf = flops / (us_s1 * 1e-6) / 1e12
+        res["roofline"].update({"bound": "mfma" if w.kv_dtype == "bf16" else "alu", "achieved": round(tf, 2),
+                                "peak": peak_tf, "unit": "TFLOP/s", "frac": round(tf / peak_tf, 4),
+                                "hbm_gbs": round(ach, 1)})
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, kv_bytes, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -10,8 +10,9 @@
 // through a ring of LDS tiles (one barrier per block), or KW key streams that
 // take the split's 32-key blocks in turn with their own tile and running max
 // / sum / accumulators, merged at the end.  Shapes, by rows per KV head:
-//   * 64+ (wide MLA), 32 (draft groups): 4 or 2 tiles on a ring of 4 (three
-//     blocks in flight), each block read once per 64 or 32 rows;
+//   * 64+ (wide MLA; prefill, where every query position of a GQA group is
+//     a row), 32 (draft groups): 4 or 2 tiles on a ring of 4 (three blocks
+//     in flight), each block read once per 64 or 32 rows;
 //   * 16 (MLA bh16): one tile, four key streams, load -> wait -> compute;
 //   * 1-15 (GQA, MLA with few heads): one wave alone on a ring of 3 (two
 //     blocks in flight); 25 KB of LDS at head dim 64 and 49 KB at 128 (two
@@ -168,7 +169,11 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
 
   const WgCoord wc = wg_coord((uint32_t)logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap), p.fd_tiles, p.head_tiles,
                               p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch);
-  const int tile = wc.tile, kvh = wc.kvh, b = wc.b, s = wc.s;
+  // Causal rows: later head tiles hold later query positions, which see more
+  // keys, so they are handed out first (longest work first; the numbering
+  // is a relabelling and changes no result).
+  const int tile = p.causal ? p.head_tiles - 1 - wc.tile : wc.tile;
+  const int kvh = wc.kvh, b = wc.b, s = wc.s;
 
   // The workgroup's last query row (rows differ in visible length only with
   // causal drafts; every row of a workgroup belongs to one request).
@@ -637,8 +642,10 @@ constexpr Entry kTable[] = {
     mk<256, 256, false, 2, 1>(32),
     mk<256, 256, false, 1, 4>(16),
     mk<256, 256, false, 1, 1>(1),
+    mk<128, 128, false, 4, 1>(64),
     mk<128, 128, false, 1, 4>(16),
     mk<128, 128, false, 1, 1>(1),
+    mk<64, 64, false, 4, 1>(64),
     mk<64, 64, false, 1, 4>(16),
     mk<64, 64, false, 1, 1>(1),
 };

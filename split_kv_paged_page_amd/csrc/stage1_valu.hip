@@ -76,7 +76,11 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
 
   const WgCoord wc = wg_coord((uint32_t)logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap), p.fd_tiles, p.head_tiles,
                               p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch);
-  const int tile = wc.tile, kvh = wc.kvh, b = wc.b, s = wc.s;
+  // Causal rows: later head tiles hold later query positions, which see more
+  // keys, so they are handed out first (longest work first; the numbering
+  // is a relabelling and changes no result).
+  const int tile = p.causal ? p.head_tiles - 1 - wc.tile : wc.tile;
+  const int kvh = wc.kvh, b = wc.b, s = wc.s;
 
   const int L = p.ctx[b];
   int sb, se;

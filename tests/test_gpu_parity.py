@@ -42,6 +42,9 @@ def small_cases():
         "mla_h4": scaled("mla_b48", context_lens=(3000, 1, 2100), num_q_heads=4, prefix_len=0, prefix_group=0,
                          seed=29),
         "gqa_d64_bf16": scaled("gqa_64k_d64", context_lens=(4100, 1, 700), seed=32),
+        # causal prefill: every token a query row, shorter sequences right-aligned
+        "prefill_small_d64": scaled("prefill_varlen_d64", context_lens=(300, 129, 64, 1), q_len=300, seed=34),
+        "prefill_small_d128": scaled("prefill_2048x4_d128", context_lens=(257, 257), q_len=257, seed=35),
         # fp32 runs on the vector ALUs: 8 and 16 rows at head dim 128
         "gqa_f32_g8": scaled("gqa_64k", context_lens=(3000, 1, 777), kv_dtype="f32", seed=28),
         "gqa_f32_g16": scaled("gqa_64k", context_lens=(2100, 300), num_q_heads=32, kv_dtype="f32", seed=31),
@@ -120,6 +123,7 @@ def test_parity_rising_and_peaked_scores(name, top, q_gain):
 
 
 @pytest.mark.parametrize("name,splits", [("gqa_tiny_f32", (1, 2, 4, 7, 16)),
+                                         ("prefill_small_d64", (1, 2, 5)),
                                          ("gqa_64k_s5000", (1, 3, 64, 79, 200, 300)),
                                          ("gqa_g6_bf16", (1, 17, 40)),
                                          ("gqa_f32_g16", (1, 9, 33)),
@@ -370,7 +374,8 @@ def test_stage2_alone_on_random_partials(S, Hq, dtype):
 
 # ---- full sizes, policy split count (the launch configuration the benchmark times) ----
 
-FULL = [("gqa_64k", None), ("gqa_64k_d64", None), ("varlen_drafts", None), ("mla_b48", (0, 13, 47)),
+FULL = [("gqa_64k", None), ("gqa_64k_d64", None), ("varlen_drafts", None), ("prefill_2048x4_d64", None),
+        ("prefill_varlen_d128", None), ("mla_b48", (0, 13, 47)),
         ("mla_wide", (0, 63)), ("mla_b48_ctl", (5, 40))]
 
 

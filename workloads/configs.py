@@ -1,6 +1,6 @@
 """Workload shapes for split-KV paged decode.
 
-Six workloads stand in for the traffic the pages measure:
+Workloads that stand in for the traffic the pages measure:
 
 * ``gqa_tiny_f32``   - tiny fp32 GQA decode (4 query heads over 1 KV head,
   head dim 64, 256 keys in 16 pages of 16, fixed 4 splits).
@@ -22,6 +22,14 @@ Six workloads stand in for the traffic the pages measure:
 * ``gqa_64k_d64``    - the 64K GQA shape at head dim 64, bf16: the head dim
   whose 128-byte K rows rocm-libraries PR #10102 pads in LDS (Motivation
   bank table).
+* ``prefill_2048x4_d64`` / ``prefill_varlen_d64`` (and ``_d128``) - causal
+  prefill attention, the step before decode, at the two batches the same
+  PR's varlen sweep drives (Technical Details, launcher-cache paragraph):
+  4 sequences of 2,048 tokens, and 6 of 256-2,048.  Every token of a
+  sequence is a query row; the query block has max_s = 2,048 rows per
+  sequence and a shorter sequence's tokens are its last rows (the earlier
+  rows see no key and return 0 / -inf).  16 query heads over 4 KV heads
+  (one of the PR's GQA ratios), page size 16.
 
 The MLA batch-48 pool: six distinct 63,240-key prefixes plus 48 private
 4,760-key suffixes need 607,920 distinct slots, more than a 400k-token pool
@@ -127,6 +135,15 @@ def _mk() -> dict:
         name="varlen_drafts", batch=6, q_len=4, num_q_heads=32, num_kv_heads=4,
         head_dim_qk=256, head_dim_v=256, page_size=16, kv_dtype="bf16",
         context_lens=(256, 512, 768, 1024, 1536, 2048), pool_pages=768, causal=True, seed=5)
+    for d in (64, 128):
+        c[f"prefill_2048x4_d{d}"] = Workload(
+            name=f"prefill_2048x4_d{d}", batch=4, q_len=2048, num_q_heads=16, num_kv_heads=4,
+            head_dim_qk=d, head_dim_v=d, page_size=16, kv_dtype="bf16",
+            context_lens=(2048,) * 4, pool_pages=1024, causal=True, seed=7)
+        c[f"prefill_varlen_d{d}"] = Workload(
+            name=f"prefill_varlen_d{d}", batch=6, q_len=2048, num_q_heads=16, num_kv_heads=4,
+            head_dim_qk=d, head_dim_v=d, page_size=16, kv_dtype="bf16",
+            context_lens=(256, 512, 768, 1024, 1536, 2048), pool_pages=768, causal=True, seed=8)
     c["gqa_64k_d64"] = Workload(
         name="gqa_64k_d64", batch=1, q_len=1, num_q_heads=16, num_kv_heads=2,
         head_dim_qk=64, head_dim_v=64, page_size=16, kv_dtype="bf16",
