@@ -223,10 +223,12 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   bounds(L, sb, se, end_max);
   const bool guess_ok = em_g > sb_g && sb_g == sb && em_g == end_max;
 
-  // This lane's query row and its visible end.
+  // This lane's query row and its visible end.  Rows past the group are
+  // never written; they score every key (their end is unbounded), so they
+  // never keep a block on the masked path.
   const int gr = (tile * RW + rw) * 16 + n;
   const bool row_ok = gr < p.rows_total;
-  int row_end = sb;
+  int row_end = 0x7fffffff;
   if (row_ok) {
     const int j = (int)fdiv((uint32_t)gr, p.fd_group);
     const int nv = p.causal ? L - p.q_len + 1 + j : L;
@@ -339,11 +341,20 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   // Scores of query row n for keys 4g+i and 16+4g+i (log2 units, masked),
   // and their max over the row's 32 keys.
   auto scores = [&](int blk, const f32x4_t& st0, const f32x4_t& st1, float* sc) {
+    if (__all(blk + 32 <= row_end)) {
+      // every key of the block is visible to every row: no mask
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k0 = blk + 4 * g + i, k1 = blk + 16 + 4 * g + i;
-      sc[i] = k0 < row_end ? st0[i] * p.scale_log2 : kNegInf;
-      sc[4 + i] = k1 < row_end ? st1[i] * p.scale_log2 : kNegInf;
+      for (int i = 0; i < 4; ++i) {
+        sc[i] = st0[i] * p.scale_log2;
+        sc[4 + i] = st1[i] * p.scale_log2;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k0 = blk + 4 * g + i, k1 = blk + 16 + 4 * g + i;
+        sc[i] = k0 < row_end ? st0[i] * p.scale_log2 : kNegInf;
+        sc[4 + i] = k1 < row_end ? st1[i] * p.scale_log2 : kNegInf;
+      }
     }
     float bm = sc[0];
 #pragma unroll
@@ -356,9 +367,12 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   // (s%4) of key 4g + s/4 (first read) or 16 + 4g + s/4 (second read).
   auto pv = [&](const uint8_t* vtile, const float* sc) {
     const uint32_t vt = lds_addr(vtile);
+    // A row whose reference is still -inf has only -inf scores; subtracting
+    // 0 instead gives exp2(-inf) = 0 without a test per score.
+    const float ms = m == kNegInf ? 0.f : m;
     float pw[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pw[e] = sc[e] == kNegInf ? 0.f : fast_exp2(sc[e] - m);
+    for (int e = 0; e < 8; ++e) pw[e] = fast_exp2(sc[e] - ms);
 #pragma unroll
     for (int e = 0; e < 8; ++e) l += pw[e];
     uint4 pk;
