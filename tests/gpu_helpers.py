@@ -32,12 +32,14 @@ def validate_inputs(inp):
 class Decode:
     """One uploaded problem + plan; run() calls attn_decode_run."""
 
-    def __init__(self, inp, num_splits=0, flags=0, max_splits=None, max_context_len=None):
+    def __init__(self, inp, num_splits=0, flags=0, max_splits=None, max_context_len=None, relayout=None):
         import torch
         validate_inputs(inp)
         self.inp = inp
         w = inp.w
         self.t = upload(inp, "cuda")
+        if relayout is not None:     # other strides for the same cache contents
+            self.t = relayout(self.t)
         t = self.t
         self.desc = sk.make_desc_from_tensors(t["q"], t["k_cache"], t["v_cache"], t["page_table"],
                                               head_dim_v=w.head_dim_v, causal=w.causal)

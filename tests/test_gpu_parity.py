@@ -163,6 +163,60 @@ def test_plan_sized_for_longer_contexts(name, extra):
         check_against_oracle(d, tol_for(w))
 
 
+@pytest.mark.parametrize("base,P", [("gqa_64k", P) for P in (1, 2, 4, 8, 32, 128)] +
+                         [("varlen_drafts", 4), ("varlen_drafts", 64), ("mla_b48", 4),
+                          ("gqa_tiny_f32", 1), ("gqa_tiny_f32", 4), ("gqa_tiny_f32", 64)])
+def test_parity_page_sizes(base, P):
+    """Every power-of-two page size the page walk's shift/mask serves, on
+    each kernel shape (ragged contexts, so pages end part-filled)."""
+    kw = dict(prefix_len=0, prefix_group=0) if base == "mla_b48" else {}
+    ctx = (300, 1, 777) if base != "varlen_drafts" else (256, 515, 1030)
+    w = scaled(base, context_lens=ctx, page_size=P, seed=40 + P, **kw)
+    inp = generate(w)
+    say(f"page size {base} P={P}")
+    d = Decode(inp, num_splits=w.num_splits).run()
+    check_against_oracle(d, tol_for(w))
+
+
+def _strided(kind):
+    """Re-lay the cache tensors out with other strides and NaN in every
+    element the kernels must not read."""
+    def f(t):
+        import torch
+        out = dict(t)
+        for key in ("k_cache", "v_cache"):
+            c = t[key]
+            if c is None:
+                continue
+            if kind == "padded":        # token pitch = D + 64 elements
+                big = torch.full((*c.shape[:3], c.shape[3] + 64), float("nan"), dtype=c.dtype, device=c.device)
+                big[..., :c.shape[3]] = c
+                out[key] = big[..., :c.shape[3]]
+            else:                       # token-major pages: [pages, P, H_kv, D]
+                tm = torch.full((c.shape[0], c.shape[2], c.shape[1], c.shape[3]), float("nan"), dtype=c.dtype,
+                                device=c.device)
+                tm.copy_(c.permute(0, 2, 1, 3))
+                out[key] = tm.permute(0, 2, 1, 3)
+        return out
+    return f
+
+
+@pytest.mark.parametrize("name", ["gqa_64k_s5000", "varlen_drafts", "mla_b4_private", "gqa_tiny_f32",
+                                  "prefill_small_d64"])
+@pytest.mark.parametrize("kind", ["padded", "token_major"])
+def test_parity_strided_pools(name, kind):
+    """The same cache contents under other element strides (the descriptor
+    carries page, head and token strides): a padded token pitch whose padding
+    is NaN, and a token-major page layout."""
+    cases = dict(small_cases(), mla_b4_private=scaled("mla_b48", context_lens=(3000, 1, 2100, 4097), prefix_len=0,
+                                                      prefix_group=0))
+    w = cases[name]
+    inp = inputs(name, w) if name in small_cases() else generate(w)
+    say(f"strided {name} {kind}")
+    d = Decode(inp, num_splits=w.num_splits, relayout=_strided(kind)).run()
+    check_against_oracle(d, tol_for(w))
+
+
 def test_empty_contexts_and_splits():
     w = scaled("gqa_64k", context_lens=(0, 5, 64, 65, 0, 130), pool_pages=64, seed=9)
     inp = generate(w)
