@@ -33,7 +33,8 @@
  *   v_cache      same with v_strides; when v_aliases_k, V is K[..., :Dv] and
  *                v_cache must equal k_cache
  *   page_table   int32 [B, max_pages_per_req] row-major; entries past
- *                ceil(ctx/P) are never read
+ *                ceil(ctx/P) are never used (a single-request plan may read,
+ *                and then ignore, entries up to ceil(max_context_len/P))
  *   context_lens int32 [B]
  *   out          [B, q_len, H_q, Dv] contiguous, dtype
  *   lse          float [B, q_len, H_q] (optional)

@@ -46,7 +46,7 @@ struct Stage2Params {
   int32_t rows;           // B * q_len * Hq
   int32_t num_splits;
   int32_t head_dim_v;
-  FastDiv fd_cols;        // head_dim_v / 4 (row-major merge)
+  FastDiv fd_cols;        // head_dim_v / 4 (output pair -> row, column)
 };
 
 // Stage-1 launchers; return false when no kernel exists for the shape.
