@@ -47,9 +47,11 @@
  * kernels on `stream` (a hipStream_t; NULL = the null stream) and return
  * without synchronising, so they may be captured into a HIP graph.  Device
  * data (page ids, context lengths) is not validated: page ids must lie in
- * [0, num_pages) and 0 <= ctx <= max_pages_per_req * P (ctx >= q_len when
- * causal), or the kernels read out of bounds.  The plan is a plain struct the
- * caller owns and may copy.
+ * [0, num_pages) and 0 <= ctx <= max_pages_per_req * P, or the kernels read
+ * out of bounds.  With causal rows and ctx < q_len, the first q_len - ctx
+ * rows see no key and return 0 / -inf (a varlen prefill batch right-aligns
+ * each sequence this way).  The plan is a plain struct the caller owns and
+ * may copy.
  *
  * Errors: every call returns an attn_status; the thread-local text of the
  * last failure is attn_decode_last_error().  No call aborts the process.
