@@ -8,8 +8,10 @@ KV pool is replicated R times and step i reads replica i mod R, so every step
 reads KV that no cache still holds (R x touched bytes >= 1 GiB, four times the
 last-level cache).  The K timed steps run as one captured HIP graph
 (launch overhead excluded) bracketed by torch.cuda.synchronize(); HIP events
-on the launch stream give the time.  Stage 1 alone is timed the same way
-(a graph of K stage-1 launches) for the roofline entry.
+on the launch stream give the time.  The graph is replayed five times and
+the median replay is reported (every replay's figure is in the line).  Stage
+1 alone is timed the same way (a graph of K stage-1 launches) for the
+roofline entry.
 
 Prints one JSON line.  value = logical KV bytes per op / time per op (GB/s).
 """
@@ -92,7 +94,8 @@ def time_eager(fn_steps, steps, stream):
             fn_steps(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1), None
+    ms = e0.elapsed_time(e1)
+    return ms, None, [ms]
 
 
 def copy_probe(mib):
@@ -109,24 +112,31 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 20}), flush=True)
 
 
-def time_graph(fn_steps, steps, stream):
-    """Capture fn_steps(i) for i < steps into one graph; return (ms total)."""
+def time_graph(fn_steps, steps, stream, rounds=5):
+    """Capture fn_steps(i) for i < steps into one graph; replay it `rounds`
+    times, each between HIP events; return (median ms per replay, graph,
+    every replay's ms)."""
+    import statistics
+
     import torch
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for i in range(steps):
             fn_steps(i)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    times = []
     with torch.cuda.stream(stream):     # replay() launches on the current stream
         g.replay()                      # untimed replay (graph upload, first touches)
         torch.cuda.synchronize()
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1), g
+        for _ in range(rounds):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+    return statistics.median(times), g, times
 
 
 def cpu_baseline(inp, kv_bytes, budget_s):
@@ -203,9 +213,9 @@ def main():
     torch.cuda.synchronize()
 
     timer = time_eager if args.eager else time_graph
-    ms, g = timer(step, args.steps, stream)
+    ms, g, op_rounds = timer(step, args.steps, stream)
     del g
-    ms1, g1 = timer(stage1, args.steps, stream)
+    ms1, g1, s1_rounds = timer(stage1, args.steps, stream)
     del g1
     us_op = ms * 1e3 / args.steps
     us_s1 = ms1 * 1e3 / args.steps
@@ -233,6 +243,9 @@ def main():
         "us_per_op": round(us_op, 3),
         "kv_hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
         "stage1_us": round(us_s1, 3),
+        "rounds": len(op_rounds),
+        "us_per_op_rounds": [round(x * 1e3 / args.steps, 3) for x in op_rounds],
+        "stage1_us_rounds": [round(x * 1e3 / args.steps, 3) for x in s1_rounds],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.kv_dtype == "bf16" else "f32",
         "accumulate": "f32",

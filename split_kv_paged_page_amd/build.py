@@ -1,6 +1,7 @@
 """Build libsplitkv.so in-tree with hipcc for gfx950.
 
     python -m split_kv_paged_page_amd.build
+    python -m split_kv_paged_page_amd.build --resource-usage   # also print per-kernel registers / LDS
 
 Every HIP source is compiled with packed-FP32 instructions disabled: the
 compiler then never forms v_pk_{add,mul,fma}_f32 from scalar float code.
@@ -32,23 +33,58 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, usage: list | None = None) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if usage is not None else []
+    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    noise = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
-    if noise:
-        sys.stderr.write("\n".join(noise) + "\n")
+    lines = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+    if usage is not None:
+        import re
+        usage.extend(ln for ln in lines if "kernel-resource-usage" in ln)
+        # drop the remarks and the source excerpts the compiler prints under them
+        lines = [ln for ln in lines if "kernel-resource-usage" not in ln and not re.match(r"^\s*\d*\s*\|", ln)]
+    if lines:
+        sys.stderr.write("\n".join(lines) + "\n")
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def resource_table(remarks: list) -> list:
+    """(kernel, VGPRs, AGPRs, spilled VGPRs, LDS bytes, waves per SIMD) from the
+    compiler's kernel-resource-usage remarks."""
+    import re
+    rows, cur = [], None
+    for ln in remarks:
+        m = re.search(r"Function Name: (\S+)", ln)
+        if m:
+            cur = {"kernel": _demangle(m.group(1))}
+            rows.append(cur)
+            continue
+        for key, pat in (("vgpr", r" VGPRs: (\d+)"), ("agpr", r"AGPRs: (\d+)"), ("spill", r"VGPRs Spill: (\d+)"),
+                         ("lds", r"LDS Size \[bytes/block\]: (\d+)"), ("occ", r"Occupancy \[waves/SIMD\]: (\d+)")):
+            m = re.search(pat, ln)
+            if m and cur is not None and key not in cur:
+                cur[key] = int(m.group(1))
+    return rows
+
+
+def _demangle(name: str) -> str:
+    try:
+        r = subprocess.run(["c++filt", name], capture_output=True, text=True)
+        out = r.stdout.strip() or name
+    except OSError:
+        out = name
+    return out.replace("splitkv::(anonymous namespace)::", "").replace("(splitkv::Stage1Params)", "").replace(
+        "(splitkv::Stage2Params)", "")
+
+
+def build(verbose: bool = False, usage: list | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, usage), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,4 +97,13 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--resource-usage" in sys.argv:
+        remarks: list = []
+        build(verbose=True, usage=remarks)
+        print("| kernel | VGPRs | AGPRs | spilled VGPRs | LDS bytes | waves / SIMD |")
+        print("|---|---|---|---|---|---|")
+        for r in resource_table(remarks):
+            print(f"| `{r['kernel']}` | {r.get('vgpr', '')} | {r.get('agpr', '')} | {r.get('spill', '')} | "
+                  f"{r.get('lds', '')} | {r.get('occ', '')} |")
+    else:
+        build(verbose=True)

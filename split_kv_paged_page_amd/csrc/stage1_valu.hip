@@ -345,7 +345,7 @@ constexpr Entry entry() {
 
 constexpr Entry kTable[] = {
     entry<64, 64, 4>(),  entry<64, 64, 8>(),  entry<64, 64, 16>(),
-    entry<128, 128, 4>(), entry<128, 128, 8>(), entry<128, 128, 16>(),
+    entry<128, 128, 4>(), entry<128, 128, 8>(),   // 16 rows at 128 would spill: two 8-row tiles
 };
 
 const Entry* find(int dtype, int dk, int dv, int rt) {

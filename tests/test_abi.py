@@ -119,7 +119,7 @@ def test_kernel_choice_by_rows_per_kv_head():
         (dict(Hq=16, Hkv=2, Dk=256, Dv=256), (M, 16, 1)), # 8 rows at head dim 256
         (dict(Hq=8, dtype=F32), (V, 4, 4)),               # fp32 stays on the vector ALUs
         (dict(Hq=16, dtype=F32), (V, 8, 4)),
-        (dict(Hq=32, dtype=F32), (V, 16, 4)),
+        (dict(Hq=32, dtype=F32), (V, 8, 4)),              # 16 rows: two 8-row tiles at head dim 128
         (dict(Hq=4, Hkv=1, Dk=64, Dv=64, dtype=F32), (V, 4, 4)),
     ]
     for kw, want in cases:
