@@ -11,8 +11,8 @@
 // take the split's 32-key blocks in turn with their own tile and running max
 // / sum / accumulators, merged at the end.  Shapes, by rows per KV head:
 //   * 64+ (wide MLA; prefill, where every query position of a GQA group is
-//     a row), 32 (draft groups): 4 or 2 tiles on a ring of 4 (three blocks
-//     in flight), each block read once per 64 or 32 rows;
+//     a row), 32 (draft groups): 4 or 2 tiles on a ring of 3 (two blocks in
+//     flight), each block read once per 64 or 32 rows;
 //   * 16 (MLA bh16): one tile, four key streams, load -> wait -> compute;
 //   * 1-15 (GQA, MLA with few heads): one wave alone on a ring of 3 (two
 //     blocks in flight); 25 KB of LDS at head dim 64 and 49 KB at 128 (two
@@ -67,9 +67,12 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 template <int DK, int DV, bool VALIAS, int RW, int KW>
 struct MCfg {
   static constexpr int NW = RW * KW;               // waves: RW row tiles x KW key streams
-  // Ring depth: 4 tiles for shared row tiles, 3 for a lone wave (measured
-  // faster than 4 there), none for key streams (one tile each).
-  static constexpr int NBUF = RW > 1 ? 4 : KW == 1 ? 3 : 1;
+  // Ring depth: 3 tiles (two blocks in flight while one is computed) for
+  // shared row tiles and a lone wave; none for key streams (one tile each).
+  // Measured against 4 tiles: lone wave (64K GQA) 15.7 / 16.4 us, drafts
+  // 13.6 / 14.4, prefill 4 x 2048 at head dim 128 139 / 162 (the smaller
+  // ring also lets a third workgroup onto the CU), wide MLA 379 / 380.
+  static constexpr int NBUF = KW == 1 ? 3 : 1;
   static constexpr int KCH = DK * 2 / 16;          // 16-byte chunks of a K row
   static constexpr int VCH = DV * 2 / 16;          // 16-byte chunks of a V row
   static constexpr int KK = DK / 32;               // Q.K MFMA steps
