@@ -336,6 +336,10 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
         lds_wait2<2 * ahead>(r0, r1);
         st0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r0), qb[kk], st0, 0, 0, 0);
         st1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r1), qb[kk], st1, 0, 0, 0);
+        // Keep the step's MFMAs right after its wait: left alone, the
+        // scheduler sinks them below the later steps' waits, so the reads no
+        // longer overlap the matrix cores.
+        __builtin_amdgcn_sched_barrier(0);
       };
       (step(std::integral_constant<int, I>{}), ...);
     }(std::make_integer_sequence<int, C::KK>{});
@@ -409,6 +413,7 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
         lds_wait2<2 * ahead>(r0, r1);
         const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);   // as in Q.K
       };
       (step(std::integral_constant<int, I>{}), ...);
     }(std::make_integer_sequence<int, C::DT>{});

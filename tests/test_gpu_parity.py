@@ -45,6 +45,9 @@ def small_cases():
         # causal prefill: every token a query row, shorter sequences right-aligned
         "prefill_small_d64": scaled("prefill_varlen_d64", context_lens=(300, 129, 64, 1), q_len=300, seed=34),
         "prefill_small_d128": scaled("prefill_2048x4_d128", context_lens=(257, 257), q_len=257, seed=35),
+        # 80 and 120 rows per KV head: a second head tile with 16 and 56 rows
+        "prefill_q20_d64": scaled("prefill_varlen_d64", context_lens=(300, 20, 77), q_len=20, seed=36),
+        "prefill_q30_d128": scaled("prefill_2048x4_d128", context_lens=(500, 30), q_len=30, seed=37),
         # fp32 runs on the vector ALUs: 8 and 16 rows at head dim 128
         "gqa_f32_g8": scaled("gqa_64k", context_lens=(3000, 1, 777), kv_dtype="f32", seed=28),
         "gqa_f32_g16": scaled("gqa_64k", context_lens=(2100, 300), num_q_heads=32, kv_dtype="f32", seed=31),
