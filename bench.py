@@ -14,6 +14,12 @@ the median replay is reported (every replay's figure is in the line).  Stage
 roofline entry.
 
 Prints one JSON line.  value = logical KV bytes per op / time per op (GB/s).
+
+Beside stage 1 the line carries a plain device-memory read timed the same
+way (libsplitkv_probe.so): a 2 GiB streaming read, the part's practical read
+rate, and cold reads of exactly the workload's KV byte count, which pay the
+same launch, start-up and tail costs as stage 1 with no page walk and no
+arithmetic.
 """
 
 from __future__ import annotations
@@ -32,6 +38,7 @@ HBM_PEAK_GBS = 8000.0
 # vector ALUs (the fp32 kernel).
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 VALU_F32_PEAK_TFLOPS = 157.3
+PROBE_GRIDS = (1024, 2048, 4096)   # read-probe workgroup counts tried (256 lanes each); the fastest is used
 
 
 def parse():
@@ -44,6 +51,7 @@ def parse():
     ap.add_argument("--flags", type=int, default=0, help="attn_decode_plan flags")
     ap.add_argument("--replicas", type=int, default=0, help="KV pool copies to rotate (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true", help="skip the plain device-memory read beside stage 1")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step eagerly instead of from a captured graph (counter runs)")
@@ -137,6 +145,38 @@ def time_graph(fn_steps, steps, stream, rounds=5):
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1))
     return statistics.median(times), g, times
+
+
+def read_probe_line(kv_bytes, steps, stream):
+    """Plain device-memory reads timed like stage 1 (graph replays, median of
+    five): a 2 GiB streaming read at each grid of PROBE_GRIDS, then, at the
+    fastest grid, `steps` cold reads of kv_bytes each, rotating over copies
+    that together exceed 1 GiB."""
+    import torch
+    from split_kv_paged_page_amd.read_probe import read_probe
+    sink = torch.zeros(max(PROBE_GRIDS), dtype=torch.int32, device="cuda")
+    sid = stream.cuda_stream
+    big_n = 1 << 31
+    big = torch.empty(big_n // 4, dtype=torch.int32, device="cuda")
+    big_gbs = {}
+    for wgs in PROBE_GRIDS:
+        ms, g, _ = time_graph(lambda i: read_probe(big.data_ptr(), big_n, wgs, sink.data_ptr(), sid), 4, stream)
+        del g
+        big_gbs[wgs] = big_n * 4 / (ms * 1e-3) / 1e9
+    del big
+    wgs = max(big_gbs, key=big_gbs.get)
+    n = -(-kv_bytes // 256) * 256
+    R = max(1, -(-(1 << 30) // n))
+    pool = torch.empty(R * n // 4, dtype=torch.int32, device="cuda")
+    base = pool.data_ptr()
+    ms, g, _ = time_graph(lambda i: read_probe(base + (i % R) * n, n, wgs, sink.data_ptr(), sid), steps, stream)
+    del g, pool
+    same_us = ms * 1e3 / steps
+    return {"kernel": "plain read: each workgroup one contiguous share, 16 B per lane, 8 loads in flight",
+            "workgroups": wgs, "large_read_bytes": big_n, "large_read_gbs": round(big_gbs[wgs], 1),
+            "large_read_gbs_by_grid": {str(k): round(v, 1) for k, v in big_gbs.items()},
+            "same_bytes": n, "same_bytes_copies": R, "same_bytes_cold_us": round(same_us, 3),
+            "same_bytes_gbs": round(n / (same_us * 1e-6) / 1e9, 1)}
 
 
 def cpu_baseline(inp, kv_bytes, budget_s):
@@ -267,6 +307,13 @@ def main():
         res["roofline"].update({"bound": "mfma" if w.kv_dtype == "bf16" else "alu", "achieved": round(tf, 2),
                                 "peak": peak_tf, "unit": "TFLOP/s", "frac": round(tf / peak_tf, 4),
                                 "hbm_gbs": round(ach, 1)})
+    if not args.no_read_probe:
+        rp = read_probe_line(kv_bytes, args.steps, stream)
+        # stage 1 against a bare read: its time relative to a cold read of
+        # the same KV bytes, and its rate relative to the streaming read
+        rp["same_bytes_us_over_stage1_us"] = round(rp["same_bytes_cold_us"] / us_s1, 4)
+        rp["stage1_gbs_over_large_read_gbs"] = round(ach / rp["large_read_gbs"], 4)
+        res["read_probe"] = rp
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, kv_bytes, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -58,9 +58,25 @@ class AttnDecodePlan(ctypes.Structure):
 _lib = None
 
 
+def one_hip_runtime() -> None:
+    """Import torch, when installed, before a HIP library of this package is
+    opened.  torch ships its own libamdhip64.so and asks for it by the name
+    libamdhip64.so, while the libraries here are linked against the soname
+    libamdhip64.so.7: opened first, a library here would map the system HIP
+    runtime and torch would then map its own, leaving two runtimes in the
+    process, and a kernel launched through one on memory the other allocated
+    fails.  With torch loaded first, its runtime carries the soname the
+    libraries ask for and the process keeps one runtime."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+
+
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
+        one_hip_runtime()
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m split_kv_paged_page_amd.build` (hipcc, gfx950)")

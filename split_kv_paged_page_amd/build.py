@@ -1,7 +1,8 @@
-"""Build libsplitkv.so in-tree with hipcc for gfx950.
+"""Build libsplitkv.so (the decode library) and libsplitkv_probe.so (a plain
+device-memory read the benchmark times beside it) in-tree with hipcc for gfx950.
 
     python -m split_kv_paged_page_amd.build
-    python -m split_kv_paged_page_amd.build --resource-usage   # also print per-kernel registers / LDS
+    python -m split_kv_paged_page_amd.build --resource-usage   # also print the decode kernels' registers / LDS
 
 Every HIP source is compiled with packed-FP32 instructions disabled: the
 compiler then never forms v_pk_{add,mul,fma}_f32 from scalar float code.
@@ -22,6 +23,8 @@ LIB = os.path.join(HERE, "libsplitkv.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["host.cpp", "stage1_valu.hip", "stage1_mfma.hip", "stage2.hip"]
+PROBE_SRC = os.path.join(HERE, "probe", "read_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libsplitkv_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -37,7 +40,7 @@ def _compile(src: str, usage: list | None = None) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
     extra = ["-Rpass-analysis=kernel-resource-usage"] if usage is not None else []
-    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]   # src may be absolute
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -81,18 +84,25 @@ def _demangle(name: str) -> str:
         "(splitkv::Stage2Params)", "")
 
 
-def build(verbose: bool = False, usage: list | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda src: _compile(src, usage), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    shutil.move(tmp, LIB)
+    shutil.move(tmp, out)
+
+
+def build(verbose: bool = False, usage: list | None = None) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        jobs = [ex.submit(_compile, src, usage) for src in SOURCES]
+        probe = ex.submit(_compile, PROBE_SRC)
+        objs = [j.result() for j in jobs]
+        _link([probe.result()], PROBE_LIB)
+    _link(objs, LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
