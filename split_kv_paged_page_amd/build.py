@@ -22,7 +22,11 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsplitkv.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["host.cpp", "stage1_valu.hip", "stage1_mfma.hip", "stage2.hip"]
+SOURCES = ["host.cpp", "stage1_valu.hip", "stage1_mfma.hip", "stage1_mfma_mla.hip", "stage2.hip"]
+# Per-file options.  The matrix-core shapes at head dims 64-256 take MFMA
+# results in VGPRs instead of AGPRs (stage1_mfma.hip says why and what it
+# measured); the MLA shapes do not.
+FILE_FLAGS = {"stage1_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 PROBE_SRC = os.path.join(HERE, "probe", "read_probe.hip")
 PROBE_LIB = os.path.join(HERE, "libsplitkv_probe.so")
 
@@ -40,6 +44,7 @@ def _compile(src: str, usage: list | None = None) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"]
     extra = ["-Rpass-analysis=kernel-resource-usage"] if usage is not None else []
+    extra += FILE_FLAGS.get(os.path.basename(src), [])
     cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]   # src may be absolute
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -49,7 +54,8 @@ def _compile(src: str, usage: list | None = None) -> str:
         import re
         usage.extend(ln for ln in lines if "kernel-resource-usage" in ln)
         # drop the remarks and the source excerpts the compiler prints under them
-        lines = [ln for ln in lines if "kernel-resource-usage" not in ln and not re.match(r"^\s*\d*\s*\|", ln)]
+        lines = [ln for ln in lines if "kernel-resource-usage" not in ln and not re.match(r"^\s*\d*\s*\|", ln)
+                 and not ln.startswith("In file included from")]
     if lines:
         sys.stderr.write("\n".join(lines) + "\n")
     return obj
