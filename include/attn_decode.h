@@ -144,7 +144,8 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
  * num_splits = 0 uses plan->num_splits; any value in [1, plan->max_splits]
  * is allowed (results agree up to float rounding).  workspace_bytes must be
  * at least the size attn_decode_workspace_layout reports for that split
- * count.  scale multiplies q.k before the softmax.
+ * count.  scale multiplies q.k before the softmax; it must be positive and
+ * finite (with scale * log2(e) finite too), else ATTN_EINVAL.
  */
 attn_status attn_decode_run(const attn_decode_plan_t* plan, const void* q,
                             const void* k_cache, const void* v_cache,

@@ -126,7 +126,13 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   if (d.v_aliases_k && v != k) return fail(ATTN_EINVAL, "aliased V: v_cache must equal k_cache");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) % 16 || (uintptr_t)ws % 256)
     return fail(ATTN_EINVAL, "q/k/v must be 16-byte aligned and the workspace 256-byte aligned");
-  if (!(scale == scale)) return fail(ATTN_EINVAL, "scale is NaN");
+  // The kernels keep raw dot products and apply scale * log2(e) to the
+  // block maximum and inside the weights' FMA, which needs a positive,
+  // finite factor (a negative one would turn the maximum into a minimum,
+  // zero would turn masked scores into NaN).
+  const float scale_log2 = scale * 1.4426950408889634f;
+  if (!(scale > 0.f) || !(scale_log2 <= 3.4028234663852886e38f))
+    return fail(ATTN_EINVAL, "scale must be positive and finite (got %g)", (double)scale);
   int64_t o_off, l_off, need;
   layout(plan, S, &o_off, &l_off, &need);
   if (ws_bytes < need)
@@ -142,7 +148,7 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   p.ctx = ctx;
   p.o_part = (float*)((char*)ws + o_off);
   p.lse_part = (float*)((char*)ws + l_off);
-  p.scale_log2 = scale * 1.4426950408889634f;
+  p.scale_log2 = scale_log2;
   p.batch = d.batch;
   p.q_len = d.q_len;
   p.num_q_heads = d.num_q_heads;

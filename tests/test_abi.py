@@ -239,6 +239,13 @@ def test_run_argument_errors_before_any_launch():
     with pytest.raises(sk.AttnDecodeError) as ei:
         sk.attn_decode_run(p, fake + 8, fake, fake, fake, fake, 0.1, 0, fake, None, fake, 1 << 30, stream=0)
     assert ei.value.status == sk.ATTN_EINVAL
-    with pytest.raises(sk.AttnDecodeError) as ei:
-        sk.attn_decode_run(p, fake, fake, fake, fake, fake, float("nan"), 0, fake, None, fake, 1 << 30, stream=0)
-    assert ei.value.status == sk.ATTN_EINVAL
+    # scale must be positive and finite (the kernels scale the block maximum, not each score)
+    for bad in (float("nan"), 0.0, -0.1, float("inf"), 3.0e38):
+        for call in (sk.attn_decode_run, sk.attn_decode_partials):
+            args = (p, fake, fake, fake, fake, fake, bad, 0)
+            with pytest.raises(sk.AttnDecodeError) as ei:
+                if call is sk.attn_decode_run:
+                    call(*args, fake, None, fake, 1 << 30, stream=0)
+                else:
+                    call(*args, fake, 1 << 30, stream=0)
+            assert ei.value.status == sk.ATTN_EINVAL, bad
