@@ -105,6 +105,63 @@ def test_parity_small(name):
           f"out {e_out:.2e} lse {e_lse:.2e}")
 
 
+def random_cases(n=48, seed=20261202):
+    """Seeded random shapes across the whole interface: dtype and head dims
+    (fp32 64/128, bf16 64/128/256, MLA 576/512 aliased), group sizes 1-24,
+    q_len 1-33 with and without causal rows, page sizes 1-64, batches of
+    1-4 with ragged contexts (empty ones and ones shorter than q_len
+    included), and the planner's split count or a forced one."""
+    import dataclasses
+    rng = np.random.default_rng(seed)
+    base = get("gqa_64k")
+    cases = {}
+    for i in range(n):
+        kind = rng.choice(["bf16", "bf16", "bf16", "mla", "f32"])
+        if kind == "mla":
+            dk, dv, alias, dt, hkv = 576, 512, True, "bf16", 1
+            hq = int(rng.integers(1, 41))
+            P = int(rng.choice([1, 1, 16, 64]))
+        else:
+            dk = dv = int(rng.choice([64, 128] if kind == "f32" else [64, 128, 256]))
+            alias, dt = False, ("f32" if kind == "f32" else "bf16")
+            hkv = int(rng.integers(1, 5))
+            hq = hkv * int(rng.integers(1, 25))
+            P = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+        q_len = int(rng.choice([1] * 6 + [2, 3, 4, 5, 8, 17, 33]))
+        while (hq // hkv) * q_len > 256:            # keep the oracle quick
+            q_len = max(1, q_len // 2)
+        causal = bool(q_len > 1 and rng.random() < 0.8)
+        B = int(rng.integers(1, 5))
+        ctx = rng.integers(1, 2500, B)
+        ctx[rng.random(B) < 0.15] = 0
+        small = rng.random(B) < 0.15
+        ctx[small] = rng.integers(1, q_len + 2, int(small.sum()))
+        S = int(rng.integers(1, 40)) if rng.random() < 0.4 else 0
+        need = sum(-(-int(c) // P) for c in ctx)
+        w = dataclasses.replace(base, name=f"rand{i}", batch=B, q_len=q_len, num_q_heads=hq, num_kv_heads=hkv,
+                                head_dim_qk=dk, head_dim_v=dv, page_size=P, kv_dtype=dt,
+                                context_lens=tuple(int(c) for c in ctx), pool_pages=2 * need + 3,
+                                v_aliases_k=alias, causal=causal, num_splits=S, seed=1000 + i)
+        cases[f"rand{i:02d}"] = w
+    return cases
+
+
+_RANDOM = random_cases()
+
+
+@pytest.mark.parametrize("name", list(_RANDOM))
+def test_parity_random_shapes(name):
+    w = _RANDOM[name]
+    say(f"random {name}: {w.kv_dtype} B={w.batch} q_len={w.q_len} heads={w.num_q_heads}/{w.num_kv_heads} "
+        f"dims={w.head_dim_qk}/{w.head_dim_v} P={w.page_size} causal={w.causal} ctx={w.context_lens} "
+        f"S={w.num_splits} run")
+    inp = generate(w)
+    d = Decode(inp, num_splits=w.num_splits).run()
+    e_out, e_lse = check_against_oracle(d, tol_for(w))
+    print(f"{name}: S={d.S} rows/wg={d.plan.rows_per_wg} waves={d.plan.stage1_waves} out {e_out:.2e} "
+          f"lse {e_lse:.2e}")
+
+
 @pytest.mark.parametrize("name", ["gqa_64k_s5000", "mla_b4_private", "mla_wide_b4", "varlen_drafts",
                                   "gqa_g4_bf16", "gqa_g12_bf16", "d256_g8", "mla_h4", "gqa_f32_g8", "gqa_d64_bf16"])
 @pytest.mark.parametrize("top,q_gain", [(4.0, 1.0), (1.0, 8.0), (3.0, 4.0)])
