@@ -348,9 +348,12 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   };
 
   // Dot products q.k of query row n for keys 4g+i and 16+4g+i (-inf where
-  // masked), and the row's block max in log2 units.  The scale is applied
-  // once to the max here and inside the weights' FMA below, not per score
-  // (scale > 0, so the max of the scaled scores is the scaled max).
+  // masked), and the max of this lane's eight in log2 units.  The scale is
+  // applied once to the max here and inside the weights' FMA below, not per
+  // score (scale > 0, so the max of the scaled scores is the scaled max).
+  // The row's block max (over its four lane groups) is only formed when a
+  // rescale needs it: a row needs none exactly when none of its lanes'
+  // maxima passes the reference, which every lane of the row holds.
   auto scores = [&](int blk, const f32x4_t& st0, const f32x4_t& st1, float* sc) {
     if (__all(blk + 32 <= row_end)) {
       // every key of the block is visible to every row: no mask
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
     float bm = sc[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[e]);
-    return max_xor32(max_xor16(bm)) * p.scale_log2;
+    return bm * p.scale_log2;
   };
 
   // ---- weights against the reference max m, row sum, O^T += V^T P^T ----
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
         pv(tile_v(buf), sc);
       }
       if (it < nb) {
-        rescale(bm);
+        rescale(max_xor32(max_xor16(bm)));   // the row's block max
         pv(tile_v(buf), sc);
         ++it;
       }
