@@ -354,32 +354,31 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   // The row's block max (over its four lane groups) is only formed when a
   // rescale needs it: a row needs none exactly when none of its lanes'
   // maxima passes the reference, which every lane of the row holds.
-  auto scores = [&](int blk, const f32x4_t& st0, const f32x4_t& st1, float* sc) {
-    if (__all(blk + 32 <= row_end)) {
-      // every key of the block is visible to every row: no mask
+  // The mask is applied in place on the MFMA results, and only on blocks
+  // that reach past some row's visible end: with the scores copied into an
+  // array on both paths the compiler moved every score two or three times.
+  auto scores = [&](int blk, f32x4_t& st0, f32x4_t& st1) {
+    if (!__all(blk + 32 <= row_end)) {
+      // keys 4g+i and 16+4g+i of the block are visible while below rem
+      const int rem = row_end - blk - 4 * g;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sc[i] = st0[i];
-        sc[4 + i] = st1[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k0 = blk + 4 * g + i, k1 = blk + 16 + 4 * g + i;
-        sc[i] = k0 < row_end ? st0[i] : kNegInf;
-        sc[4 + i] = k1 < row_end ? st1[i] : kNegInf;
+        st0[i] = i < rem ? st0[i] : kNegInf;
+        st1[i] = 16 + i < rem ? st1[i] : kNegInf;
       }
     }
-    float bm = sc[0];
+    float bm = st0[0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[e]);
+    for (int i = 1; i < 4; ++i) bm = fmaxf(bm, st0[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bm = fmaxf(bm, st1[i]);
     return bm * p.scale_log2;
   };
 
   // ---- weights against the reference max m, row sum, O^T += V^T P^T ----
   // Transpose reads run kLaV steps ahead: lane 16g + s addresses 4 dims
   // (s%4) of key 4g + s/4 (first read) or 16 + 4g + s/4 (second read).
-  auto pv = [&](const uint8_t* vtile, const float* sc) {
+  auto pv = [&](const uint8_t* vtile, const f32x4_t& st0, const f32x4_t& st1) {
     const uint32_t vt = lds_addr(vtile);
     // Weight 2^(s * scale_log2 - m), one FMA per score.  A row whose
     // reference is still -inf has only -inf scores; subtracting 0 instead
@@ -387,7 +386,7 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
     const float ms = m == kNegInf ? 0.f : m;
     float pw[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pw[e] = fast_exp2(fmaf(sc[e], p.scale_log2, -ms));
+    for (int e = 0; e < 8; ++e) pw[e] = fast_exp2(fmaf(e < 4 ? st0[e] : st1[e - 4], p.scale_log2, -ms));
 #pragma unroll
     for (int e = 0; e < 8; ++e) l += pw[e];
     uint4 pk;
@@ -449,23 +448,22 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   // Runs blocks [0, nb) of this wave: front(it) makes block it readable and
   // returns its tile buffer; mid(it) runs between Q.K and P.V.
   auto run_blocks = [&](int nb, auto&& front, auto&& mid) {
-    float sc[8];
+    f32x4_t st0, st1;
     float bm = kNegInf;
     int it = 0;
     while (it < nb) {
       int buf = 0;
       for (; it < nb; ++it) {
         buf = front(it);
-        f32x4_t st0, st1;
         qk(tile_k(buf), st0, st1);
-        bm = scores(blk_of(it), st0, st1, sc);
+        bm = scores(blk_of(it), st0, st1);
         mid(it);
         if (__any(bm > m + kLazyLog2)) break;
-        pv(tile_v(buf), sc);
+        pv(tile_v(buf), st0, st1);
       }
       if (it < nb) {
         rescale(max_xor32(max_xor16(bm)));   // the row's block max
-        pv(tile_v(buf), sc);
+        pv(tile_v(buf), st0, st1);
         ++it;
       }
     }
