@@ -74,7 +74,10 @@ struct MCfg {
   // Measured against 4 tiles: lone wave (64K GQA) 15.7 / 16.4 us, drafts
   // 13.6 / 14.4, prefill 4 x 2048 at head dim 128 139 / 162 (the smaller
   // ring also lets a third workgroup onto the CU), wide MLA 379 / 380.
-  static constexpr int NBUF = KW == 1 ? 3 : 1;
+  // The four-wave shape at head dim 128 (prefill, whose keys mostly come
+  // from cache) takes 2 tiles, which fits a fourth workgroup per CU: whole
+  // op 4 x 2048 132.3 -> 128.0 us, varlen 95.0 -> 90.8.
+  static constexpr int NBUF = KW == 1 ? (DK == 128 && RW == 4 ? 2 : 3) : 1;
   static constexpr int KCH = DK * 2 / 16;          // 16-byte chunks of a K row
   static constexpr int VCH = DV * 2 / 16;          // 16-byte chunks of a V row
   static constexpr int KK = DK / 32;               // Q.K MFMA steps
