@@ -297,6 +297,15 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
     S = target / per_split;
     if (S > blocks) S = blocks;
     if (S < 1) S = 1;
+    // Drop the trailing splits that would hold no key even for the longest
+    // context (the split rule rounds chunks up to 64 keys): they cost partial
+    // writes and merge reads and change no chunk.  Drafts (longest 2,048 keys,
+    // 10 -> 8 splits): 16.6 -> 16.3 us per op.
+    if (max_context_len > 0) {
+      const int64_t per = (max_context_len + (int64_t)S - 1) / S;
+      const int64_t chunk = (per + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+      S = (int)((max_context_len + chunk - 1) / chunk);
+    }
   }
   if (S > kMaxSplits) S = kMaxSplits;
   p.num_splits = S;

@@ -96,6 +96,16 @@ def test_p2_policy_reproduces_table():
         assert (e - b) // 64 == r["trips"] and (e - b) % 64 == 0
 
 
+def test_default_split_count_leaves_no_split_empty_at_the_longest_context():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        B, hkv = int(rng.integers(1, 9)), int(rng.choice([1, 2, 4, 8]))
+        L = int(rng.integers(1, 200000))
+        p = sk.attn_decode_plan(desc(B=B, Hq=hkv * int(rng.integers(1, 9)), Hkv=hkv, maxp=(L + 15) // 16), L, 0)
+        b, e = sk.attn_decode_split_range(p, L, 0, p.num_splits - 1)
+        assert e > b, (B, hkv, L, p.num_splits)        # the last split holds keys
+
+
 def test_default_policy_fills_the_chip():
     p = sk.attn_decode_plan(desc(), 65536, 0)
     wgs = p.num_splits * 1 * 2 * p.head_tiles
@@ -148,7 +158,8 @@ def test_default_split_count_fills_one_round():
     mla = dict(Hkv=1, Dk=576, Dv=512, P=1, maxp=68000, alias=1, pages=655360)
     assert sk.attn_decode_plan(desc(B=48, Hq=4, **mla), 68000, 0).num_splits == 256 // 48
     assert sk.attn_decode_plan(desc(B=48, Hq=16, **mla), 68000, 0).num_splits == 256 // 48
-    assert sk.attn_decode_plan(desc(B=6, Hq=32, Hkv=4, Dk=256, Dv=256), 2048, 0).num_splits == 256 // 24
+    # drafts: one round would be 256 // 24 = 10 splits, but 2,048 keys in 256-key chunks fill only 8
+    assert sk.attn_decode_plan(desc(B=6, Hq=32, Hkv=4, Dk=256, Dv=256), 2048, 0).num_splits == 8
 
 
 def test_plan_key_covers_shape_fields():
