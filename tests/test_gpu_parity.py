@@ -505,3 +505,37 @@ def test_parity_full_size_sampled(name, requests):
     if requests is not None:
         # every other request: outputs written, finite, lse finite
         assert not torch.isnan(d.out).any() and torch.isfinite(d.lse).all()
+
+
+@pytest.mark.parametrize("name", ["gqa_64k_s5000", "mla_b48_b16", "varlen_drafts", "prefill_small_d64", "gqa_f32_g8"])
+def test_graph_replays_match_eager(name):
+    # The calls allocate nothing and never synchronise, so they can be captured
+    # in a graph; every replay, with eager work and synchronisations between
+    # replays, must give the eager bits (output, log-sum-exp and partials).
+    import split_kv_paged_page_amd as sk
+    w = small_cases()[name]
+    inp = inputs(name, w)
+    say(f"graph {name} eager run")
+    d = Decode(inp, num_splits=w.num_splits).run()
+    e_out, e_lse, e_ws = d.out.clone(), d.lse.clone(), d.used_ws_bits()
+    t = d.t
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    d.poison()
+    torch.cuda.synchronize()
+    say(f"graph {name} capture")
+    with torch.cuda.graph(g, stream=s):
+        sk.attn_decode_run(d.plan, t["q"], t["k_cache"], d.v, t["page_table"], t["context_lens"],
+                           float(inp.scale), d.S, d.out, d.lse, d.ws, stream=s.cuda_stream)
+    for r in range(3):
+        d.poison()                       # eager work between replays
+        torch.cuda.synchronize()
+        say(f"graph {name} replay {r}")
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.out.view(torch.int16) if d.out.dtype == torch.bfloat16 else d.out.view(torch.int32),
+                           e_out.view(torch.int16) if e_out.dtype == torch.bfloat16 else e_out.view(torch.int32)), r
+        assert torch.equal(d.lse.view(torch.int32), e_lse.view(torch.int32)), r
+        if d.S > 1:
+            assert np.array_equal(d.used_ws_bits(), e_ws), r
