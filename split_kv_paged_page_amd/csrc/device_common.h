@@ -156,6 +156,18 @@ __device__ __forceinline__ WgCoord wg_coord(uint32_t lid, FastDiv fd_tiles, int 
   return WgCoord{(int)(lid - q1 * tiles), (int)(q1 - q2 * kvhs), (int)(q2 - q3 * batch), (int)q3};
 }
 
+// Causal plans: the head tile is the slowest index instead, so the tiles
+// with the latest query positions (the most keys) of every request and KV
+// head are dispatched before any shorter tile.  With the tile fastest, each
+// run of `tiles` workgroups went from longest to shortest for one request
+// and KV head, and the long tiles of the later requests started only when
+// the first round of workgroups drained, leaving a long tail.
+__device__ __forceinline__ WgCoord wg_coord_tiles_last(uint32_t lid, FastDiv fd_kvh, int kvhs, FastDiv fd_batch,
+                                                       int batch, FastDiv fd_splits, int splits) {
+  const uint32_t q1 = fdiv(lid, fd_kvh), q2 = fdiv(q1, fd_batch), q3 = fdiv(q2, fd_splits);
+  return WgCoord{(int)q3, (int)(lid - q1 * kvhs), (int)(q1 - q2 * batch), (int)(q2 - q3 * splits)};
+}
+
 // Workgroup order.  The dispatcher hands workgroup p to XCD p % 8; with the
 // remap on, XCD x receives one contiguous range of the logical (split-major)
 // order, so all requests' programs for one split land on one XCD's L2.  The

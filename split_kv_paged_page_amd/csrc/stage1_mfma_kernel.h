@@ -176,8 +176,10 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   auto tile_k = [&](int buf) { return smem + (kw * C::NBUF + buf) * C::TILE; };
   auto tile_v = [&](int buf) { return VALIAS ? tile_k(buf) : tile_k(buf) + C::KTILE; };
 
-  const WgCoord wc = wg_coord((uint32_t)logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap), p.fd_tiles, p.head_tiles,
-                              p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch);
+  const uint32_t lid = (uint32_t)logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap);
+  const WgCoord wc = p.causal ? wg_coord_tiles_last(lid, p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch, p.fd_splits,
+                                                    p.num_splits)
+                              : wg_coord(lid, p.fd_tiles, p.head_tiles, p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch);
   // Causal rows: later head tiles hold later query positions, which see more
   // keys, so they are handed out first (longest work first; the numbering
   // is a relabelling and changes no result).

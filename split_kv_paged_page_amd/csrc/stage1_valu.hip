@@ -74,8 +74,10 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
   const int x = lane & 15;
   uint8_t* wave_lds = smem + C::QB + wave * C::WAVE_B;
 
-  const WgCoord wc = wg_coord((uint32_t)logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap), p.fd_tiles, p.head_tiles,
-                              p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch);
+  const uint32_t lid = (uint32_t)logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap);
+  const WgCoord wc = p.causal ? wg_coord_tiles_last(lid, p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch, p.fd_splits,
+                                                    p.num_splits)
+                              : wg_coord(lid, p.fd_tiles, p.head_tiles, p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch);
   // Causal rows: later head tiles hold later query positions, which see more
   // keys, so they are handed out first (longest work first; the numbering
   // is a relabelling and changes no result).
