@@ -270,42 +270,47 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
 
   const uint8_t* kbase = (const uint8_t*)p.k + (int64_t)kvh * p.ks_head * 2;
   const uint8_t* vbase = (const uint8_t*)p.v + (int64_t)kvh * p.vs_head * 2;
-  const int64_t ks_page16 = p.ks_page * 2 / 16, ks_tok16 = p.ks_tok * 2 / 16;
-  const int64_t vs_page16 = p.vs_page * 2 / 16, vs_tok16 = p.vs_tok * 2 / 16;
+  // Strides in 16-byte units.  32-bit arithmetic is exact: the host keeps
+  // every row of the pool below 2^32 units from its head's base.
+  const uint32_t ks_page16 = (uint32_t)(p.ks_page * 2 / 16), ks_tok16 = (uint32_t)(p.ks_tok * 2 / 16);
+  const uint32_t vs_page16 = (uint32_t)(p.vs_page * 2 / 16), vs_tok16 = (uint32_t)(p.vs_tok * 2 / 16);
 
   // DMA lane mapping: instruction i moves key (i%2)*16 + lane/4, the 4 chunks
   // (i/2)*4 + ((lane%4) ^ swz(key)); its LDS slot is i*64 + lane.  With
   // RW waves on one stream, wave rw issues instructions rw, rw + RW, ...
   const int dkey0 = lane >> 2, dkey1 = 16 + (lane >> 2);
   const int dsw0 = (lane & 3) ^ tile_swz(dkey0), dsw1 = (lane & 3) ^ tile_swz(dkey1);
-  // page0 / page1: page ids of keys blk + dkey0 and blk + dkey1 (clamped to
-  // the last visible key like every other key).
+  static_assert(RW == 1 || RW % 2 == 0, "row-tile waves: one, or an even count");
+  // Row of key t (clamped to the last visible key like every other key) in
+  // page `page`, in 16-byte units from the head's base.
+  auto row16 = [&](int t, int page, uint32_t pstride, uint32_t tstride) {
+    const int tc = t < end_max ? t : end_max - 1;
+    return (uint32_t)page * pstride + (uint32_t)(tc & (P - 1)) * tstride;
+  };
+  // Moves block blk (page0 / page1: page ids of keys blk + dkey0 and
+  // blk + dkey1) into tile buffer buf.  Each lane forms one source address
+  // per key it moves and steps through the chunk groups at constant offsets,
+  // which the loads carry as immediates.
+  auto issue_dma_from = [&](const uint8_t* base, uint32_t pstride, uint32_t tstride, uint8_t* tile, int nins,
+                            int blk, int page0, int page1) {
+    if constexpr (RW % 2 == 0) {
+      // Instruction i = rw + ii*RW always moves key dkey(rw % 2), chunk group
+      // rw/2 + ii*RW/2: one source row per lane.
+      const bool odd = rw & 1;
+      const uint8_t* src = base + ((uint64_t)row16(blk + (odd ? dkey1 : dkey0), odd ? page1 : page0, pstride, tstride) +
+                                   (rw >> 1) * 4 + (odd ? dsw1 : dsw0)) * 16;
+#pragma unroll
+      for (int ii = 0; ii < nins / RW; ++ii) lds_dma16(src + ii * (RW / 2) * 64, tile + (rw + ii * RW) * 1024);
+    } else {
+      const uint8_t* src0 = base + ((uint64_t)row16(blk + dkey0, page0, pstride, tstride) + dsw0) * 16;
+      const uint8_t* src1 = base + ((uint64_t)row16(blk + dkey1, page1, pstride, tstride) + dsw1) * 16;
+#pragma unroll
+      for (int i = 0; i < nins; ++i) lds_dma16(((i & 1) ? src1 : src0) + (i >> 1) * 64, tile + i * 1024);
+    }
+  };
   auto issue_dma = [&](int blk, int page0, int page1, int buf) {
-    const int t0 = blk + dkey0, t1 = blk + dkey1;
-    const int s0 = (t0 < end_max ? t0 : end_max - 1) & (P - 1);
-    const int s1 = (t1 < end_max ? t1 : end_max - 1) & (P - 1);
-    const uint32_t k0 = (uint32_t)(page0 * ks_page16 + s0 * ks_tok16);
-    const uint32_t k1 = (uint32_t)(page1 * ks_page16 + s1 * ks_tok16);
-    uint8_t* kt = tile_k(buf);
-#pragma unroll
-    for (int ii = 0; ii < C::KINS / RW; ++ii) {
-      const int i = rw + ii * RW;
-      const uint32_t ko = (i & 1) ? k1 : k0;
-      const int ch = (i >> 1) * 4 + ((i & 1) ? dsw1 : dsw0);
-      lds_dma16(kbase + (uint64_t)ko * 16 + ch * 16, kt + i * 1024);
-    }
-    if constexpr (!VALIAS) {
-      const uint32_t v0 = (uint32_t)(page0 * vs_page16 + s0 * vs_tok16);
-      const uint32_t v1 = (uint32_t)(page1 * vs_page16 + s1 * vs_tok16);
-      uint8_t* vt = tile_v(buf);
-#pragma unroll
-      for (int ii = 0; ii < C::VINS / RW; ++ii) {
-        const int i = rw + ii * RW;
-        const uint32_t vo = (i & 1) ? v1 : v0;
-        const int ch = (i >> 1) * 4 + ((i & 1) ? dsw1 : dsw0);
-        lds_dma16(vbase + (uint64_t)vo * 16 + ch * 16, vt + i * 1024);
-      }
-    }
+    issue_dma_from(kbase, ks_page16, ks_tok16, tile_k(buf), C::KINS, blk, page0, page1);
+    if constexpr (!VALIAS) issue_dma_from(vbase, vs_page16, vs_tok16, tile_v(buf), C::VINS, blk, page0, page1);
   };
 
   // This lane's LDS byte offsets inside a tile.  Q.K step kk reads chunk
