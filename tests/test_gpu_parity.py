@@ -105,7 +105,7 @@ def test_parity_small(name):
           f"out {e_out:.2e} lse {e_lse:.2e}")
 
 
-def random_cases(n=48, seed=20261202):
+def random_cases(n=48, seed=20261202, max_ctx=2500, max_batch=4, max_splits=39, max_rows=256):
     """Seeded random shapes across the whole interface: dtype and head dims
     (fp32 64/128, bf16 64/128/256, MLA 576/512 aliased), group sizes 1-24,
     q_len 1-33 with and without causal rows, page sizes 1-64, batches of
@@ -128,15 +128,15 @@ def random_cases(n=48, seed=20261202):
             hq = hkv * int(rng.integers(1, 25))
             P = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
         q_len = int(rng.choice([1] * 6 + [2, 3, 4, 5, 8, 17, 33]))
-        while (hq // hkv) * q_len > 256:            # keep the oracle quick
+        while (hq // hkv) * q_len > max_rows:       # keep the oracle quick
             q_len = max(1, q_len // 2)
         causal = bool(q_len > 1 and rng.random() < 0.8)
-        B = int(rng.integers(1, 5))
-        ctx = rng.integers(1, 2500, B)
+        B = int(rng.integers(1, max_batch + 1))
+        ctx = rng.integers(1, max_ctx, B)
         ctx[rng.random(B) < 0.15] = 0
         small = rng.random(B) < 0.15
         ctx[small] = rng.integers(1, q_len + 2, int(small.sum()))
-        S = int(rng.integers(1, 40)) if rng.random() < 0.4 else 0
+        S = int(rng.integers(1, max_splits + 1)) if rng.random() < 0.4 else 0
         need = sum(-(-int(c) // P) for c in ctx)
         w = dataclasses.replace(base, name=f"rand{i}", batch=B, q_len=q_len, num_q_heads=hq, num_kv_heads=hkv,
                                 head_dim_qk=dk, head_dim_v=dv, page_size=P, kv_dtype=dt,
@@ -146,7 +146,11 @@ def random_cases(n=48, seed=20261202):
     return cases
 
 
-_RANDOM = random_cases()
+# 48 shapes with short contexts, then 32 with long contexts, bigger batches
+# and split counts up to 300
+_RANDOM = dict(random_cases(),
+               **{k.replace("rand", "long"): v for k, v in
+                  random_cases(n=32, seed=20261203, max_ctx=20000, max_batch=8, max_splits=300, max_rows=64).items()})
 
 
 @pytest.mark.parametrize("name", list(_RANDOM))
