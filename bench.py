@@ -205,8 +205,8 @@ def cpu_baseline(inp, kv_bytes, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU split of the path is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); the decode path does not "
+              "shard across GPUs here", file=sys.stderr)
         sys.exit(2)
     import torch
 

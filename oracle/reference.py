@@ -21,7 +21,7 @@ oracle writes that definition out directly in float64:
 and, for the per-split check, the same formulas restricted to each split's
 key range, plus the log-sum-exp merge of such partials.
 
-Readings where the pages are silent (each is also listed in the design doc):
+Readings where the pages are silent:
 * a request's query row j (of q_len) sees keys [0, L - q_len + 1 + j) when
   causal (bottom-right alignment; the context length counts the draft
   tokens), all L keys otherwise;
