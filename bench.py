@@ -235,6 +235,8 @@ def main():
     ws = torch.empty(plan.workspace_bytes // 4, dtype=torch.float32, device="cuda")
     scale = float(inp.scale)
     stream = torch.cuda.Stream()
+    # the in-kernel merge's counters start at zero (a no-op for other plans)
+    sk.attn_decode_workspace_init(plan, ws, stream=stream.cuda_stream)
 
     def step(i):
         r = i % R
@@ -295,7 +297,8 @@ def main():
                    "page_size": w.page_size, "context": (w.context_lens[0] if len(set(w.context_lens)) == 1
                                                         else list(w.context_lens)),
                    "num_splits": S, "rows_per_wg": plan.rows_per_wg, "head_tiles": plan.head_tiles,
-                   "stage1_waves": plan.stage1_waves, "xcd_remap": plan.xcd_remap, "replicas": R,
+                   "stage1_waves": plan.stage1_waves, "xcd_remap": plan.xcd_remap, "plan_flags": plan.flags,
+                   "replicas": R,
                    "kv_bytes_per_op": kv_bytes, "parallelism": "single GPU"},
         "tflops_per_s": round(flops / (us_op * 1e-6) / 1e12, 2),
         "roofline": {"bound": "hbm", "kernel": "stage1", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,

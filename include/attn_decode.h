@@ -40,7 +40,10 @@
  *   lse          float [B, q_len, H_q] (optional)
  *   workspace    float o_part [B, q_len, H_q, S, Dv] at o_part_offset and
  *                float lse_part [B, q_len, H_q, S] at lse_part_offset
- *                (attn_decode_workspace_layout), S = the run's split count
+ *                (attn_decode_workspace_layout), S = the run's split count;
+ *                a plan made with ATTN_PLAN_FUSED_MERGE also keeps one
+ *                uint32 counter per (request, KV head, head tile) at offset 0,
+ *                before o_part
  *
  * Threading and ownership: the library keeps no device memory and allocates
  * nothing; run/partials/merge only validate host-side arguments, enqueue
@@ -80,7 +83,16 @@ typedef enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
 enum {
   ATTN_PLAN_POLICY_P2 = 1,          /* split count = max(1, 256 / batch), the policy the
                                        aiter PR's per-lever table was measured at */
-  ATTN_PLAN_NO_XCD_REMAP = 2        /* keep the plain (split-minor) workgroup order */
+  ATTN_PLAN_NO_XCD_REMAP = 2,       /* keep the plain (split-minor) workgroup order */
+  ATTN_PLAN_FUSED_MERGE = 4         /* run merges in stage 1 when 2 <= S <= 64: the workgroup
+                                       that finishes a row group's last split merges the group,
+                                       so no second launch waits on an idle part (aiter PR
+                                       #4758, Motivation, batch-1 paragraph).  Matrix-core
+                                       plans only; the workspace counters need
+                                       attn_decode_workspace_init.  Off by default: on
+                                       MI355X the per-XCD L2 write-back each workgroup's
+                                       release costs, and the merge on one CU per group,
+                                       outweigh the launch it saves */
 };
 
 /* Kernel families the planner picks from. */
@@ -144,7 +156,10 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
  * num_splits = 0 uses plan->num_splits; any value in [1, plan->max_splits]
  * is allowed (results agree up to float rounding).  workspace_bytes must be
  * at least the size attn_decode_workspace_layout reports for that split
- * count.  scale multiplies q.k before the softmax; it must be positive and
+ * count.  With ATTN_PLAN_FUSED_MERGE and 2 <= S <= 64 the merge runs inside
+ * the stage-1 launch (same results up to float rounding; the workspace must
+ * have been through attn_decode_workspace_init); other split counts take the
+ * two launches.  scale multiplies q.k before the softmax; it must be positive and
  * finite (with scale * log2(e) finite too), else ATTN_EINVAL.
  */
 attn_status attn_decode_run(const attn_decode_plan_t* plan, const void* q,
@@ -172,6 +187,21 @@ attn_status attn_decode_merge(const attn_decode_plan_t* plan, int32_t num_splits
 attn_status attn_decode_workspace_layout(const attn_decode_plan_t* plan, int32_t num_splits,
                                          int64_t* o_part_offset, int64_t* lse_part_offset,
                                          int64_t* bytes);
+
+/*
+ * Makes a workspace ready for runs of this plan: with ATTN_PLAN_FUSED_MERGE,
+ * enqueues on `stream` one small kernel that zeroes the row-group counters
+ * at the start of the workspace (no memset, so it may be captured); for
+ * other plans it does nothing.  Call it once after allocating a workspace
+ * (or after using it with another plan): every fused run finds the counters
+ * zero and leaves them zero.  A fused run on counters that are not zero
+ * writes a wrong output without any error, and two runs that share a
+ * workspace must not overlap in time (the same holds for the partials).
+ * ATTN_EINVAL for a null or misaligned workspace, ATTN_EWORKSPACE if it is
+ * smaller than the counters.
+ */
+attn_status attn_decode_workspace_init(const attn_decode_plan_t* plan, void* workspace,
+                                       int64_t workspace_bytes, void* stream);
 
 /* The split rule: [*begin, *end) of split `split` of `num_splits` (0 = the
  * plan's) for a request with context_len keys.  Pure host function. */

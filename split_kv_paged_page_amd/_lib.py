@@ -19,10 +19,12 @@ ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP = range(5)
 ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_PLAN_POLICY_P2 = 1
 ATTN_PLAN_NO_XCD_REMAP = 2
+ATTN_PLAN_FUSED_MERGE = 4
 ATTN_VARIANT_VALU, ATTN_VARIANT_MFMA = 1, 2
 
 EXPORTED = ["attn_decode_plan", "attn_decode_run", "attn_decode_partials", "attn_decode_merge",
-            "attn_decode_workspace_layout", "attn_decode_split_range", "attn_decode_last_error"]
+            "attn_decode_workspace_layout", "attn_decode_workspace_init", "attn_decode_split_range",
+            "attn_decode_last_error"]
 
 _STATUS = {ATTN_OK: "ATTN_OK", ATTN_EINVAL: "ATTN_EINVAL", ATTN_EUNSUPPORTED: "ATTN_EUNSUPPORTED",
            ATTN_EWORKSPACE: "ATTN_EWORKSPACE", ATTN_EHIP: "ATTN_EHIP"}
@@ -88,6 +90,7 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_partials.argtypes = [P(AttnDecodePlan), vp, vp, vp, vp, vp, f32, i32, vp, i64, vp]
         L.attn_decode_merge.argtypes = [P(AttnDecodePlan), i32, vp, i64, vp, vp, vp]
         L.attn_decode_workspace_layout.argtypes = [P(AttnDecodePlan), i32, P(i64), P(i64), P(i64)]
+        L.attn_decode_workspace_init.argtypes = [P(AttnDecodePlan), vp, i64, vp]
         L.attn_decode_split_range.argtypes = [P(AttnDecodePlan), i32, i32, i32, P(i32), P(i32)]
         L.attn_decode_last_error.argtypes = []
         L.attn_decode_last_error.restype = ctypes.c_char_p
@@ -166,6 +169,13 @@ def attn_decode_workspace_layout(plan, num_splits: int = 0) -> tuple:
     _check(lib().attn_decode_workspace_layout(ctypes.byref(plan), num_splits, ctypes.byref(o),
                                               ctypes.byref(l_), ctypes.byref(b)))
     return o.value, l_.value, b.value
+
+
+def attn_decode_workspace_init(plan, workspace, workspace_bytes=None, stream=None):
+    """Zero the in-kernel merge's counters of a workspace (a no-op for plans
+    without ATTN_PLAN_FUSED_MERGE); once per workspace before its first run."""
+    wb = workspace_bytes if workspace_bytes is not None else _nbytes(workspace)
+    _check(lib().attn_decode_workspace_init(ctypes.byref(plan), _ptr(workspace), wb, _stream(stream)))
 
 
 def attn_decode_split_range(plan, context_len: int, num_splits: int, split: int) -> tuple:

@@ -99,13 +99,23 @@ int pick_rows_per_wg(int dtype, int dk, int dv, int rows) {
 
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
+// Row groups of the in-kernel merge: one counter per (request, KV head,
+// head tile), i.e. per set of stage-1 workgroups that differ only in split.
+int64_t counter_count(const attn_decode_plan_t* p) {
+  if (!(p->flags & ATTN_PLAN_FUSED_MERGE)) return 0;
+  return (int64_t)p->desc.batch * p->desc.num_kv_heads * p->head_tiles;
+}
+
+// [counters (fused plans)] [o_part] [lse_part], each 256-byte aligned; the
+// counters come first so that their place does not depend on S.
 void layout(const attn_decode_plan_t* p, int S, int64_t* o_off, int64_t* l_off, int64_t* bytes) {
   const attn_decode_desc& d = p->desc;
   const int64_t rows = (int64_t)d.batch * d.q_len * d.num_q_heads;
+  const int64_t cb = align256(counter_count(p) * 4);
   const int64_t ob = align256(rows * S * d.head_dim_v * 4);
-  if (o_off) *o_off = 0;
-  if (l_off) *l_off = ob;
-  if (bytes) *bytes = ob + align256(rows * S * 4);
+  if (o_off) *o_off = cb;
+  if (l_off) *l_off = cb + ob;
+  if (bytes) *bytes = cb + ob + align256(rows * S * 4);
 }
 
 attn_status resolve_splits(const attn_decode_plan_t* p, int32_t num_splits, int* S) {
@@ -120,7 +130,7 @@ attn_status resolve_splits(const attn_decode_plan_t* p, int32_t num_splits, int*
 attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q, const void* k,
                            const void* v, const int32_t* pt, const int32_t* ctx, float scale,
                            void* ws, int64_t ws_bytes, hipStream_t st, void* out = nullptr,
-                           float* lse_out = nullptr) {
+                           float* lse_out = nullptr, void* fin_out = nullptr, float* fin_lse = nullptr) {
   const attn_decode_desc& d = plan->desc;
   if (!q || !k || !v || !pt || !ctx || !ws) return fail(ATTN_EINVAL, "a device pointer is null");
   if (d.v_aliases_k && v != k) return fail(ATTN_EINVAL, "aliased V: v_cache must equal k_cache");
@@ -141,6 +151,11 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   splitkv::Stage1Params p{};
   p.out = out;
   p.lse_out = lse_out;
+  if (fin_out) {   // in-kernel merge: counters at the workspace's start
+    p.counters = (uint32_t*)ws;
+    p.fin_out = fin_out;
+    p.fin_lse = fin_lse;
+  }
   p.q = q;
   p.k = k;
   p.v = v;
@@ -234,7 +249,7 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
     return fail(ATTN_EINVAL, "max_context_len %d exceeds max_pages_per_req * page_size", max_context_len);
   if (num_splits < 0 || num_splits > kMaxSplits)
     return fail(ATTN_EINVAL, "num_splits must be in [0, %d]", kMaxSplits);
-  if (flags & ~(ATTN_PLAN_POLICY_P2 | ATTN_PLAN_NO_XCD_REMAP))
+  if (flags & ~(ATTN_PLAN_POLICY_P2 | ATTN_PLAN_NO_XCD_REMAP | ATTN_PLAN_FUSED_MERGE))
     return fail(ATTN_EINVAL, "unknown plan flags 0x%x", flags);
 
   const attn_decode_desc& d = *desc;
@@ -275,6 +290,8 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
     p.stage1_waves = 4;
   }
   p.head_tiles = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
+  if ((flags & ATTN_PLAN_FUSED_MERGE) && p.variant != ATTN_VARIANT_MFMA)
+    return fail(ATTN_EUNSUPPORTED, "the in-kernel merge needs the matrix-core stage 1 (bf16)");
 
   // Split count.  The aiter PR's launcher gives each request about 256 /
   // batch splits so that the 256 CUs stay busy (Motivation; Test Result
@@ -337,6 +354,20 @@ attn_status attn_decode_workspace_layout(const attn_decode_plan_t* plan, int32_t
   return ATTN_OK;
 }
 
+attn_status attn_decode_workspace_init(const attn_decode_plan_t* plan, void* workspace, int64_t workspace_bytes,
+                                       void* stream) {
+  if (!plan) return fail(ATTN_EINVAL, "plan is null");
+  const int64_t n = counter_count(plan);
+  if (n == 0) return ATTN_OK;
+  if (!workspace || (uintptr_t)workspace % 256) return fail(ATTN_EINVAL, "workspace must be 256-byte aligned");
+  if (workspace_bytes < n * 4)
+    return fail(ATTN_EWORKSPACE, "workspace of %lld bytes is below the %lld counter bytes", (long long)workspace_bytes,
+                (long long)(n * 4));
+  hipError_t e = splitkv::launch_zero_u32((uint32_t*)workspace, n, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "counter fill launch");
+  return ATTN_OK;
+}
+
 attn_status attn_decode_split_range(const attn_decode_plan_t* plan, int32_t context_len, int32_t num_splits,
                                     int32_t split, int32_t* begin, int32_t* end) {
   if (!begin || !end) return fail(ATTN_EINVAL, "begin/end is null");
@@ -386,6 +417,9 @@ attn_status attn_decode_run(const attn_decode_plan_t* plan, const void* q, const
   if (S == 1)  // one split: stage 1 writes the final output itself
     return enqueue_stage1(plan, S, q, k_cache, v_cache, page_table, context_lens, scale, workspace,
                           workspace_bytes, (hipStream_t)stream, out, lse);
+  if ((plan->flags & ATTN_PLAN_FUSED_MERGE) && S <= splitkv::kFusedMaxSplits)
+    return enqueue_stage1(plan, S, q, k_cache, v_cache, page_table, context_lens, scale, workspace,
+                          workspace_bytes, (hipStream_t)stream, nullptr, nullptr, out, lse);
   st = enqueue_stage1(plan, S, q, k_cache, v_cache, page_table, context_lens, scale, workspace,
                       workspace_bytes, (hipStream_t)stream);
   if (st != ATTN_OK) return st;

@@ -36,7 +36,16 @@ struct Stage1Params {
   FastDiv fd_tiles, fd_kvh, fd_batch, fd_splits, fd_group;
   int32_t align_shift;
   int32_t guess_ctx;      // > 0: likely context length of every request (early page-table reads)
+  // In-kernel merge (matrix-core kernel, 2 <= num_splits <= kFusedMaxSplits):
+  // non-null counters, one per (request, KV head, head tile), zero on entry
+  // and left zero, make the workgroup that writes a row group's last split
+  // merge the group's partials into fin_out (bf16) and fin_lse (optional).
+  uint32_t* counters;
+  void* fin_out;
+  float* fin_lse;
 };
+
+constexpr int kFusedMaxSplits = 64;   // one split per lane in the merge's weight pass
 
 struct Stage2Params {
   const float* o_part;
@@ -48,6 +57,9 @@ struct Stage2Params {
   int32_t head_dim_v;
   FastDiv fd_cols;        // head_dim_v / 4 (output pair -> row, column)
 };
+
+// Zeroes n 32-bit words with a small fill kernel (no memset node in a graph).
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
 
 // Stage-1 launchers; return false when no kernel exists for the shape.
 bool stage1_valu_supported(int dtype, int dk, int dv, int rows_per_wg);

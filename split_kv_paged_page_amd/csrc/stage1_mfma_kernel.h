@@ -687,6 +687,88 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
       write_row(grr, d, o, lse);
     }
   }
+
+  // ---- In-kernel merge: the last workgroup of a row group merges it ----
+  // Every workgroup of the group (same request, KV head and head tile; one
+  // per split) releases its partials and counts itself in; the one that
+  // brings the count to S reads all S partials back and merges them as
+  // stage 2 would (weights e^(lse_s - max) / sum, natural log), then resets
+  // the counter.  Nothing waits on another workgroup, so no ordering of the
+  // grid can stall it.
+  if (p.counters) {
+    const uint32_t grp = ((uint32_t)b * p.num_kv_heads + kvh) * p.head_tiles + tile;
+    const int S = p.num_splits;
+    // Device-scope ordering costs an L2 write-back (release) and an L2
+    // invalidation (acquire) on the issuing XCD, so one lane does each, once:
+    // the barrier puts every lane's partial stores before lane 0's release
+    // count, and only the merging workgroup acquires.
+    __syncthreads();   // every lane's partials are stored; LDS is free
+    volatile int* flag = (volatile int*)smem;
+    if (threadIdx.x == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(p.counters + grp, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = prev == (uint32_t)(S - 1);
+      if (last) {
+        __hip_atomic_store(p.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other workgroups' partials, not stale lines
+      }
+      *flag = last;
+    }
+    __syncthreads();
+    if (!*flag) return;
+
+    const int nrows = last_row - first_row + 1;
+    auto out_row = [&](int r) {
+      const int grr = first_row + r;
+      const int j = (int)fdiv((uint32_t)grr, p.fd_group);
+      return ((int64_t)b * p.q_len + j) * p.num_q_heads + kvh * p.group + grr - j * p.group;
+    };
+    // Weights: one wave per row, lane s holds split s (S <= 64).
+    float* wts = (float*)(smem + 256);   // [RW * 16][64]
+    for (int r = wave; r < nrows; r += C::NW) {
+      const int64_t row = out_row(r);
+      const float x = lane < S ? p.lse_part[row * S + lane] : kNegInf;
+      const float M = max_xor32(max_xor16(row16_max(x)));
+      const float w = M == kNegInf ? 0.f : fast_exp2((x - M) * kLog2e);
+      const float den = sum_xor32(sum_xor16(row16_sum(w)));
+      wts[r * 64 + lane] = M == kNegInf ? 0.f : w * (1.f / den);
+      if (lane == 0 && p.fin_lse) p.fin_lse[row] = M == kNegInf ? kNegInf : M + __logf(den);
+    }
+    __syncthreads();
+    // Outputs: lane -> two (row, 4 dims) items at a time, eight splits of
+    // each loaded before the first is used (16 loads in flight per lane).
+    constexpr int T = 64 * C::NW, IT = 2;
+    const int items = nrows * (DV / 4);
+    for (int i0 = threadIdx.x; i0 < items; i0 += IT * T) {
+      const float* src[IT];
+      const float* wr[IT];
+      int64_t orow[IT];
+      float4 o[IT];
+#pragma unroll
+      for (int k = 0; k < IT; ++k) {
+        const int idx = i0 + k * T < items ? i0 + k * T : i0;   // a spare item repeats the first
+        const int r = idx / (DV / 4), c = idx - r * (DV / 4);
+        orow[k] = out_row(r) * DV + c * 4;
+        src[k] = p.o_part + out_row(r) * S * DV + c * 4;
+        wr[k] = wts + r * 64;
+        o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll 8
+      for (int s2 = 0; s2 < S; ++s2) {
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+          const float wv = wr[k][s2];
+          const float4 v = *(const float4*)(src[k] + (int64_t)s2 * DV);
+          o[k].x = fmaf(wv, v.x, o[k].x);
+          o[k].y = fmaf(wv, v.y, o[k].y);
+          o[k].z = fmaf(wv, v.z, o[k].z);
+          o[k].w = fmaf(wv, v.w, o[k].w);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < IT; ++k)
+        if (i0 + k * T < items) store_out4(p.fin_out, 1, orow[k], o[k]);
+    }
+  }
 }
 
 }  // namespace

@@ -138,7 +138,18 @@ void launch(const Stage2Params& p, int64_t pairs, int lp, hipStream_t st) {
   }
 }
 
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
 
 int stage2_lanes(int64_t pairs, int num_splits) {
   int lp = 1;

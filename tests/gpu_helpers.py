@@ -50,6 +50,14 @@ class Decode:
         self.S = num_splits or self.plan.num_splits
         self.dtype = torch.float32 if w.kv_dtype == "f32" else torch.bfloat16
         self.ws = torch.empty(self.plan.workspace_bytes // 4, dtype=torch.float32, device="cuda")
+        # With the in-kernel merge the workspace starts with its counters,
+        # which poisoning leaves alone; they are zeroed once here.
+        self.fused = bool(flags & sk.ATTN_PLAN_FUSED_MERGE)
+        self.counter_words = sk.attn_decode_workspace_layout(self.plan, self.S)[0] // 4 if self.fused else 0
+        if self.fused:
+            self.ws[:self.counter_words].fill_(float("nan"))   # the init call must clear them
+            sk.attn_decode_workspace_init(self.plan, self.ws)
+            torch.cuda.synchronize()
         self.out = torch.empty((w.batch, w.q_len, w.num_q_heads, w.head_dim_v), dtype=self.dtype,
                                device="cuda")
         self.lse = torch.empty((w.batch, w.q_len, w.num_q_heads), dtype=torch.float32, device="cuda")
@@ -59,8 +67,14 @@ class Decode:
     def v(self):
         return self.t["k_cache"] if self.t["v_cache"] is None else self.t["v_cache"]
 
+    def counters(self) -> np.ndarray:
+        """The in-kernel merge's counters (one per request, KV head and head tile)."""
+        w = self.inp.w
+        n = w.batch * w.num_kv_heads * self.plan.head_tiles
+        return self.ws[:n].cpu().numpy().view(np.uint32)
+
     def poison(self):
-        self.ws.fill_(float("nan"))
+        self.ws[self.counter_words:].fill_(float("nan"))
         self.out.fill_(float("nan"))
         self.lse.fill_(float("nan"))
 

@@ -190,6 +190,37 @@ def test_workspace_layout():
     assert b64 < b
 
 
+def test_fused_merge_plan_layout_and_init_checks():
+    # The in-kernel merge keeps one counter per (request, KV head, head tile)
+    # at the workspace's start; o_part and lse_part move up by that block.
+    plain = sk.attn_decode_plan(desc(B=3), 4096, 8)
+    fused = sk.attn_decode_plan(desc(B=3), 4096, 8, sk.ATTN_PLAN_FUSED_MERGE)
+    assert fused.key != plain.key and fused.variant == sk.ATTN_VARIANT_MFMA
+    counters = 3 * 2 * fused.head_tiles
+    shift = (counters * 4 + 255) // 256 * 256
+    for S in (0, 2, 5):
+        po, pl_, pb = sk.attn_decode_workspace_layout(plain, S)
+        fo, fl, fb = sk.attn_decode_workspace_layout(fused, S)
+        assert (fo, fl, fb) == (po + shift, pl_ + shift, pb + shift)
+    assert fused.workspace_bytes == plain.workspace_bytes + shift
+    # two head tiles of 16 rows (20 rows per KV head): counters per tile
+    two = sk.attn_decode_plan(desc(B=2, Hq=40, Hkv=2), 4096, 4, sk.ATTN_PLAN_FUSED_MERGE)
+    assert two.head_tiles == 2 and sk.attn_decode_workspace_layout(two, 0)[0] == 256
+    # fp32 runs on the vector ALUs, which have no in-kernel merge
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_plan(desc(dtype=sk.ATTN_F32), 4096, 8, sk.ATTN_PLAN_FUSED_MERGE)
+    assert ei.value.status == sk.ATTN_EUNSUPPORTED
+    # init: nothing to do without the flag; argument errors before any launch
+    sk.attn_decode_workspace_init(plain, None, 0, stream=0)
+    L = sk.lib()
+    assert L.attn_decode_workspace_init(ctypes.byref(fused), None, 1 << 20, None) == sk.ATTN_EINVAL
+    assert L.attn_decode_workspace_init(ctypes.byref(fused), (1 << 20) + 16, 1 << 20, None) == sk.ATTN_EINVAL
+    assert L.attn_decode_workspace_init(ctypes.byref(fused), 1 << 20, counters * 4 - 4, None) == sk.ATTN_EWORKSPACE
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_plan(desc(), 4096, 8, 8)
+    assert ei.value.status == sk.ATTN_EINVAL
+
+
 @pytest.mark.parametrize("mutate,status", [
     (dict(Hq=15), sk.ATTN_EINVAL),
     (dict(B=0), sk.ATTN_EINVAL),
