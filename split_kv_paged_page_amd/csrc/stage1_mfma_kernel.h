@@ -98,6 +98,7 @@ struct MCfg {
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   static_assert(KINS % RW == 0 && VINS % RW == 0, "DMA instructions split evenly over the row tiles");
   static_assert(RW == 1 || KW == 1, "shared tiles carry one key stream");
+  static_assert(SMEM >= 256 + RW * 16 * 64 * 4, "in-kernel merge: flag word + weights [rows][64 splits]");
   static constexpr int MINE = NBUF > 1 ? (KINS + VINS) / RW : 0;  // DMA instructions per wave per block
 };
 
