@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from tests.gpu_helpers import Decode, lse_err, row_rel_err, say, tol_for
-from tests.test_gpu_parity import check_against_oracle, inputs, small_cases
+from tests.test_gpu_parity import _RANDOM, check_against_oracle, inputs, small_cases
 from workloads import generate, get
 
 pytestmark = pytest.mark.gpu
@@ -135,3 +135,23 @@ def test_fused_full_size_sampled(name, S, requests):
     if requests is not None:
         assert not torch.isnan(d.out).any() and torch.isfinite(d.lse).all()
     print(f"{name}: S={d.S} out {e_out:.2e} lse {e_lse:.2e}")
+
+
+_RANDOM_BF16 = [k for k, w in _RANDOM.items() if w.kv_dtype == "bf16"]
+
+
+@pytest.mark.parametrize("name", _RANDOM_BF16)
+def test_fused_parity_random_shapes(name):
+    # the bf16 shapes of the two-launch random sweep (head dims 64-576, groups
+    # 1-40, causal rows, page sizes 1-64, empty and short contexts), each at
+    # its split count clamped to the fused range 2-64
+    w = _RANDOM[name]
+    inp = generate(w)
+    probe = Decode(inp, num_splits=w.num_splits)
+    S = fused_splits(probe.S)
+    say(f"fused random {name}: B={w.batch} q_len={w.q_len} heads={w.num_q_heads}/{w.num_kv_heads} "
+        f"dims={w.head_dim_qk}/{w.head_dim_v} P={w.page_size} causal={w.causal} ctx={w.context_lens} S={S}")
+    d = Decode(inp, num_splits=S, flags=FUSED).run()
+    e_out, e_lse = check_against_oracle(d, tol_for(w), S=S)
+    assert (d.counters() == 0).all()
+    print(f"{name}: S={S} rows/wg={d.plan.rows_per_wg} out {e_out:.2e} lse {e_lse:.2e}")
