@@ -85,6 +85,8 @@ def split_bounds(L: int, S: int, A: int = SPLIT_ALIGN) -> list:
 
 
 def kv_head_of(h: int, num_q_heads: int, num_kv_heads: int) -> int:
+    """KV head that query head h reads: consecutive query heads share one
+    (a GQA group of num_q_heads / num_kv_heads heads)."""
     return h // (num_q_heads // num_kv_heads)
 
 
@@ -138,8 +140,8 @@ def _request_rows(inp, b: int, kvh: int):
     """Query rows of request b that read KV head kvh, as (row index list of
     (j, h)), float64 matrix [R, Dk]."""
     w = inp.w
-    g = w.num_q_heads // w.num_kv_heads
-    idx = [(j, h) for j in range(w.q_len) for h in range(kvh * g, (kvh + 1) * g)]
+    idx = [(j, h) for j in range(w.q_len) for h in range(w.num_q_heads)
+           if kv_head_of(h, w.num_q_heads, w.num_kv_heads) == kvh]
     qr = np.stack([to_f64(inp.q[b, j, h], w.kv_dtype) for (j, h) in idx])
     return idx, qr
 

@@ -130,7 +130,7 @@ def test_fused_full_size_sampled(name, S, requests):
     assert 2 <= d.S <= 64, d.S
     say(f"fused full-size {name}: run S={d.S}")
     d.run()
-    e_out, e_lse = check_against_oracle(d, tol_for(w), requests=requests, check_splits=False)
+    e_out, e_lse = check_against_oracle(d, tol_for(w), requests=requests)
     assert (d.counters() == 0).all()
     if requests is not None:
         assert not torch.isnan(d.out).any() and torch.isfinite(d.lse).all()

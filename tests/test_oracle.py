@@ -10,8 +10,8 @@
 * the split rule against the trip counts printed in aiter PR #4758's Test
   Result tables, and against a brute-force search;
 * planted mistakes (wrong slot, dropped scale, top-left causal alignment,
-  wrong GQA head map, V read from K, flipped merge sign, log base 2) each fail
-  one of the pins above.
+  wrong GQA head map, interleaved KV-head rule, V read from K, flipped merge
+  sign, log base 2) each fail one of the pins above.
 """
 
 import math
@@ -354,6 +354,14 @@ def test_planted_gqa_head_map(monkeypatch):
         return idx, np.stack([ref.to_f64(inp.q[b, j, h], w.kv_dtype) for (j, h) in idx])
     _planted(monkeypatch, "_request_rows", bad_rows)
     assert bruteforce_error(CASES[0]) > 1e-3
+
+
+def test_planted_kv_head_of(monkeypatch):
+    # interleaved instead of consecutive groups: query head h on KV head h % H_kv
+    _planted(monkeypatch, "kv_head_of", lambda h, hq, hkv: h % hkv)
+    assert bruteforce_error(CASES[0]) > 1e-3
+    # a single KV head, or one query head per KV head, cannot tell the maps apart
+    assert bruteforce_error(CASES[5]) <= 1e-12
 
 
 def test_planted_v_from_k(monkeypatch):
