@@ -1,10 +1,13 @@
 """Seeded generation of paged-KV decode inputs (raw bits, host memory).
 
-Draw order for a workload with seed ``s`` (``numpy.random.default_rng(s)``):
-page permutation of the pool, then q, then K, then V (V is not drawn when it
-aliases K).  Values are N(0, 1) drawn as float32; bf16 workloads round them
-to bf16 with round-to-nearest-even, and both the oracle and the GPU read the
-same bf16 bit patterns.
+Streams for a workload with seed ``s``: ``numpy.random.default_rng(s)`` draws
+the page permutation of the pool, then q; the K pool is drawn in chunks of
+2^24 values, chunk c from ``default_rng([s, 1, c])``, and the V pool likewise
+from ``default_rng([s, 2, c])`` (V is not drawn when it aliases K).  The
+chunks are independent streams, so the pools (up to 3.76 GB) are filled by
+several threads with the same bits as one thread.  Values are N(0, 1) drawn
+as float32; bf16 workloads round them to bf16 with round-to-nearest-even, and
+both the oracle and the GPU read the same bf16 bit patterns.
 
 Layouts (all C-contiguous):
 
@@ -18,6 +21,8 @@ Layouts (all C-contiguous):
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, replace
 
 import numpy as np
@@ -60,6 +65,30 @@ def _normal_values(rng: np.random.Generator, shape, kv_dtype: str) -> np.ndarray
     return out.reshape(shape)
 
 
+def _normal_pool(seed: int, stream: int, shape, kv_dtype: str) -> np.ndarray:
+    """N(0, 1) values of a KV pool; chunk c of 2^24 values comes from
+    default_rng([seed, stream, c]), filled by a thread pool (NumPy's
+    generators and ufuncs release the GIL on large arrays)."""
+    n = int(np.prod(shape))
+    f32 = kv_dtype == "f32"
+    out = np.empty(n, dtype=np.float32 if f32 else np.uint16)
+
+    def fill(c):
+        s = c * _CHUNK
+        e = min(n, s + _CHUNK)
+        v = np.random.default_rng([seed, stream, c]).standard_normal(e - s, dtype=np.float32)
+        out[s:e] = v if f32 else bf16_bits_from_f32(v)
+
+    chunks = -(-n // _CHUNK)
+    if chunks <= 1:
+        for c in range(chunks):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1, chunks)) as ex:
+            list(ex.map(fill, range(chunks)))
+    return out.reshape(shape)
+
+
 def page_table_for(w: Workload, perm: np.ndarray) -> np.ndarray:
     """Assign pool pages to requests from a permutation of the pool.
 
@@ -98,10 +127,10 @@ def generate(w: Workload) -> Inputs:
     perm = rng.permutation(w.pool_pages).astype(np.int32)
     pt = page_table_for(w, perm)
     q = _normal_values(rng, (w.batch, w.q_len, w.num_q_heads, w.head_dim_qk), w.kv_dtype)
-    k = _normal_values(rng, (w.pool_pages, w.num_kv_heads, w.page_size, w.head_dim_qk), w.kv_dtype)
+    k = _normal_pool(w.seed, 1, (w.pool_pages, w.num_kv_heads, w.page_size, w.head_dim_qk), w.kv_dtype)
     v = None
     if not w.v_aliases_k:
-        v = _normal_values(rng, (w.pool_pages, w.num_kv_heads, w.page_size, w.head_dim_v), w.kv_dtype)
+        v = _normal_pool(w.seed, 2, (w.pool_pages, w.num_kv_heads, w.page_size, w.head_dim_v), w.kv_dtype)
     ctx = np.asarray(w.context_lens, dtype=np.int32)
     return Inputs(w=w, q=q, k_cache=k, v_cache=v, page_table=pt, context_lens=ctx,
                   scale=np.float32(w.scale))
