@@ -261,14 +261,20 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
   p.flags = flags;
   // XCD-contiguous order (each XCD one contiguous range of the split-major
   // order) keeps the programs that share KV on one XCD's L2 (aiter PR #4758,
-  // Technical Details item 2).  With several query positions per request
-  // (causal drafts, prefill) a request's work grows with its length, and
-  // whole requests per XCD leave XCDs idle when the lengths differ; the
-  // plain order spreads every request over all XCDs.  Measured (us per op,
-  // contiguous / plain): varlen prefill 131 / 86 (head dim 64) and 197 / 124
-  // (128); equal-length prefill 105 / 118 and 151 / 180; drafts 19.3 / 18.6.
-  // The plan does not see the lengths, so q_len > 1 takes the plain order.
-  p.xcd_remap = (flags & ATTN_PLAN_NO_XCD_REMAP) || d.q_len > 1 ? 0 : 1;
+  // Technical Details item 2, which applies it when batch > 1).  MLA batch
+  // 48 with 8-request shared prefixes, stage 1 (us, A/B/B/A in one run):
+  // contiguous 294.0 / 294.2, plain 573.8 / 572.7; L2 hit rate 78.6% against
+  // 0.4%, L2 fetch 807 MB per launch against 3.77 GB.  With one request no
+  // KV is shared and the order is neutral (64K GQA 16.14 / 15.85 against
+  // 15.92 / 15.89), so batch 1 keeps the plain order as the PR does.  With
+  // several query positions per request (causal drafts, prefill) a
+  // request's work grows with its length, and whole requests per XCD leave
+  // XCDs idle when the lengths differ; the plain order spreads every request
+  // over all XCDs.  Measured (us per op, contiguous / plain): varlen prefill
+  // 131 / 86 (head dim 64) and 197 / 124 (128); equal-length prefill 105 /
+  // 118 and 151 / 180; drafts 19.3 / 18.6.  The plan does not see the
+  // lengths, so q_len > 1 takes the plain order.
+  p.xcd_remap = (flags & ATTN_PLAN_NO_XCD_REMAP) || d.q_len > 1 || d.batch == 1 ? 0 : 1;
   // bf16 runs on the matrix cores at every group size (a 16-row tile part
   // empty still costs a fraction of the vector-ALU work per key); fp32 runs
   // on the vector ALUs.

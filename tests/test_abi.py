@@ -291,3 +291,14 @@ def test_run_argument_errors_before_any_launch():
                 else:
                     call(*args, fake, 1 << 30, stream=0)
             assert ei.value.status == sk.ATTN_EINVAL, bad
+
+
+def test_xcd_order_only_for_batched_single_position_decode():
+    """The split-major XCD-contiguous order is planned for decode batches
+    (requests that may share KV on one XCD's L2), not for one request and not
+    for several query positions per request."""
+    assert sk.attn_decode_plan(mla_desc(48), 68000, 0).xcd_remap == 1
+    assert sk.attn_decode_plan(desc(B=4, maxp=2048), 2048, 0).xcd_remap == 1
+    assert sk.attn_decode_plan(desc(B=1), 65536, 0).xcd_remap == 0
+    assert sk.attn_decode_plan(desc(B=4, q_len=4, causal=1, maxp=2048), 2048, 0).xcd_remap == 0
+    assert sk.attn_decode_plan(mla_desc(48), 68000, 0, sk.ATTN_PLAN_NO_XCD_REMAP).xcd_remap == 0
