@@ -13,7 +13,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsplitkv.so")
+# SPLITKV_LIB names another build of the same library (the CPU tests load the
+# host-sanitized build this way); by default the in-tree libsplitkv.so.
+LIB_PATH = os.environ.get("SPLITKV_LIB") or os.path.join(HERE, "libsplitkv.so")
 
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP = range(5)
 ATTN_F32, ATTN_BF16 = 0, 1

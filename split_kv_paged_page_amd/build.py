@@ -3,6 +3,7 @@ device-memory read the benchmark times beside it) in-tree with hipcc for gfx950.
 
     python -m split_kv_paged_page_amd.build
     python -m split_kv_paged_page_amd.build --resource-usage   # also print the decode kernels' registers / LDS
+    python -m split_kv_paged_page_amd.build --host-check       # host code under ASan + UBSan, for CPU tests
 
 Every HIP source is compiled with packed-FP32 instructions disabled: the
 compiler then never forms v_pk_{add,mul,fma}_f32 from scalar float code.
@@ -99,6 +100,38 @@ def _link(objs: list, out: str) -> None:
     shutil.move(tmp, out)
 
 
+# Host-side sanitizers for the CPU test tier: the same sources with the host
+# code built under AddressSanitizer and UndefinedBehaviorSanitizer (device
+# code unchanged: each flag applies to the host compilation only).  The
+# library leaves the sanitizer runtime symbols undefined; the test process
+# preloads the runtime.
+HOSTCHECK_LIB = os.path.join(BUILD, "libsplitkv_hostcheck.so")
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_hostcheck() -> str:
+    """Build _build/libsplitkv_hostcheck.so (host code sanitized) for the
+    CPU tests that run the planner and argument checks under the
+    sanitizers."""
+    out = os.path.join(BUILD, "hostcheck")
+    os.makedirs(out, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(out, "hc_" + os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *FLAGS, *HOST_SANITIZE, *FILE_FLAGS.get(src, []), "-x", "hip", "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(one, SOURCES))
+    _link(objs, HOSTCHECK_LIB)
+    return HOSTCHECK_LIB
+
+
 def build(verbose: bool = False, usage: list | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
@@ -121,5 +154,7 @@ if __name__ == "__main__":
         for r in resource_table(remarks):
             print(f"| `{r['kernel']}` | {r.get('vgpr', '')} | {r.get('agpr', '')} | {r.get('spill', '')} | "
                   f"{r.get('lds', '')} | {r.get('occ', '')} |")
+    elif "--host-check" in sys.argv:
+        print(build_hostcheck())
     else:
         build(verbose=True)
