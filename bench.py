@@ -13,7 +13,13 @@ the median replay is reported (every replay's figure is in the line).  Stage
 1 alone is timed the same way (a graph of K stage-1 launches) for the
 roofline entry.
 
-Prints one JSON line.  value = logical KV bytes per op / time per op (GB/s).
+Prints one JSON line.  value = logical KV bytes per op / time per op (GB/s)
+of the headline workload (--config, 64K GQA by default).  The default run
+also times the other decode workloads (--extra): the tiny fp32 check, MLA
+batch 48 with and without shared prefixes, the 128-head MLA and the varlen
+drafts, each under "configs" with its whole-op and stage-1 times, its own
+stage-1 roofline entry, a plain cold read of the same KV bytes (unique bytes
+where prefixes are shared) and, for shared prefixes, the unique-bytes rate.
 
 Beside stage 1 the line carries a plain device-memory read timed the same
 way (libsplitkv_probe.so): a 2 GiB streaming read, the part's practical read
@@ -47,6 +53,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="gqa_64k")
+    ap.add_argument("--extra", default=EXTRA_CONFIGS,
+                    help="comma-separated workloads timed after the headline one, each reported under "
+                         "'configs' ('' for none)")
     ap.add_argument("--splits", type=int, default=0, help="force the split count (0: planner policy)")
     ap.add_argument("--flags", type=int, default=0, help="attn_decode_plan flags")
     ap.add_argument("--replicas", type=int, default=0, help="KV pool copies to rotate (0: auto)")
@@ -179,6 +188,26 @@ def read_probe_line(kv_bytes, steps, stream):
             "same_bytes_gbs": round(n / (same_us * 1e-6) / 1e9, 1)}
 
 
+def read_probe_same_bytes(nbytes, steps, stream, wgs):
+    """Cold plain reads of nbytes each (graph replays, median of five),
+    rotating over copies that together exceed 1 GiB."""
+    import torch
+    from split_kv_paged_page_amd.read_probe import read_probe
+    sink = torch.zeros(wgs, dtype=torch.int32, device="cuda")
+    n = -(-nbytes // 256) * 256
+    R = max(1, -(-(1 << 30) // n))
+    pool = torch.empty(R * n // 4, dtype=torch.int32, device="cuda")
+    base = pool.data_ptr()
+    ms, g, _ = time_graph(lambda i: read_probe(base + (i % R) * n, n, wgs, sink.data_ptr(), stream.cuda_stream),
+                          steps, stream)
+    del g, pool
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    us = ms * 1e3 / steps
+    return {"same_bytes": n, "same_bytes_copies": R, "workgroups": wgs, "same_bytes_cold_us": round(us, 3),
+            "same_bytes_gbs": round(n / (us * 1e-6) / 1e9, 1)}
+
+
 def cpu_baseline(inp, kv_bytes, budget_s):
     import numpy as np
     import oracle
@@ -202,27 +231,27 @@ def cpu_baseline(inp, kv_bytes, budget_s):
                       f"median {med * 1e3:.1f} ms/op, host os.cpu_count()={os.cpu_count()}"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); the decode path does not "
-              "shard across GPUs here", file=sys.stderr)
-        sys.exit(2)
+# Configurations timed beside the headline one in the default run, each with
+# its own stage-1 roofline: the tiny fp32 check, MLA batch 48 with and
+# without shared prefixes, the 128-head MLA and the varlen drafts.
+EXTRA_CONFIGS = "gqa_tiny_f32,mla_b48,mla_b48_ctl,mla_wide,varlen_drafts"
+
+
+def measure(w, args, stream, splits=0, flags=0, want_inputs=False):
+    """Plan, upload and time one workload: the whole op and stage 1 alone,
+    each as graph replays over cold KV.  Returns (summary dict, inputs or
+    None); every device buffer is released before returning."""
     import torch
 
-    if args.copy_probe:
-        copy_probe(args.copy_probe)
-        return
     import split_kv_paged_page_amd as sk
-    from workloads import generate, get
+    from workloads import generate
     from workloads.torch_io import upload
 
-    w = get(args.config)
     inp = generate(w)
     t = upload(inp, "cuda")
     desc = sk.make_desc_from_tensors(t["q"], t["k_cache"], t["v_cache"], t["page_table"],
                                      head_dim_v=w.head_dim_v, causal=w.causal)
-    plan = sk.attn_decode_plan(desc, int(max(w.context_lens)), args.splits or w.num_splits, args.flags)
+    plan = sk.attn_decode_plan(desc, int(max(w.context_lens)), splits or w.num_splits, flags)
     S = plan.num_splits
     kv_bytes, alg_bytes = algorithmic_bytes(w, S)
     touched = w.unique_kv_bytes()
@@ -234,7 +263,6 @@ def main():
     lse = torch.empty((w.batch, w.q_len, w.num_q_heads), dtype=torch.float32, device="cuda")
     ws = torch.empty(plan.workspace_bytes // 4, dtype=torch.float32, device="cuda")
     scale = float(inp.scale)
-    stream = torch.cuda.Stream()
     # the in-kernel merge's counters start at zero (a no-op for other plans)
     sk.attn_decode_workspace_init(plan, ws, stream=stream.cuda_stream)
 
@@ -259,6 +287,10 @@ def main():
     del g
     ms1, g1, s1_rounds = timer(stage1, args.steps, stream)
     del g1
+    del ks, vs, t, out, lse, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
     us_op = ms * 1e3 / args.steps
     us_s1 = ms1 * 1e3 / args.steps
     kv_gbs = kv_bytes / (us_op * 1e-6) / 1e9
@@ -270,24 +302,75 @@ def main():
 
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"stage1_traffic_{w.name}.json")
-    if os.path.exists(tfile):
+    if os.path.exists(tfile) and not args.eager:
         with open(tfile) as f:
             tr = json.load(f)
         if tr.get("plan_key") == str(plan.key) and tr.get("kernel_source_hash") == source_hash():
             traffic = tr.get("bytes_per_launch")
 
     res = {
+        "workload": w.name,
+        "us_per_op": round(us_op, 3),
+        "stage1_us": round(us_s1, 3),
+        "kv_gbs": round(kv_gbs, 1),
+        "kv_hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
+        "us_per_op_rounds": [round(x * 1e3 / args.steps, 3) for x in op_rounds],
+        "stage1_us_rounds": [round(x * 1e3 / args.steps, 3) for x in s1_rounds],
+        "tflops_per_s": round(flops / (us_op * 1e-6) / 1e12, 2),
+        "num_splits": S, "rows_per_wg": plan.rows_per_wg, "head_tiles": plan.head_tiles,
+        "stage1_waves": plan.stage1_waves, "xcd_remap": plan.xcd_remap, "plan_flags": plan.flags,
+        "replicas": R, "kv_bytes_per_op": kv_bytes,
+        "roofline": {"bound": "hbm", "kernel": "stage1", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": flops,
+                     "launch_us": round(us_s1, 3)},
+    }
+    if compute_bound:
+        tf = flops / (us_s1 * 1e-6) / 1e12
+        res["roofline"].update({"bound": "mfma" if w.kv_dtype == "bf16" else "alu", "achieved": round(tf, 2),
+                                "peak": peak_tf, "unit": "TFLOP/s", "frac": round(tf / peak_tf, 4),
+                                "hbm_gbs": round(ach, 1)})
+    if touched != kv_bytes:
+        # shared prefixes: the logical rate counts every request's prefix
+        # read (the re-reads come from cache); the unique bytes are what HBM
+        # must deliver at least once
+        res["unique_kv_bytes_per_op"] = touched
+        res["stage1_unique_kv_gbs"] = round(touched / (us_s1 * 1e-6) / 1e9, 1)
+        res["stage1_unique_kv_frac"] = round(touched / (us_s1 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    return res, (inp if want_inputs else None)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); the decode path does not "
+              "shard across GPUs here", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    from workloads import get
+
+    stream = torch.cuda.Stream()
+    w = get(args.config)
+    head, inp = measure(w, args, stream, args.splits, args.flags, want_inputs=not args.no_cpu_baseline)
+    kv_bytes = head["kv_bytes_per_op"]
+    us_op, us_s1 = head["us_per_op"], head["stage1_us"]
+
+    res = {
         "metric": "split-KV decode: µs per decode op and KV GB/s as % of MI355X HBM peak",
-        "value": round(kv_gbs, 1),
+        "value": head["kv_gbs"],
         "unit": "GB/s (logical KV bytes per decode op / whole-op time)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(us_op / 1e3, 6),
-        "us_per_op": round(us_op, 3),
-        "kv_hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
-        "stage1_us": round(us_s1, 3),
-        "rounds": len(op_rounds),
-        "us_per_op_rounds": [round(x * 1e3 / args.steps, 3) for x in op_rounds],
-        "stage1_us_rounds": [round(x * 1e3 / args.steps, 3) for x in s1_rounds],
+        "us_per_op": us_op,
+        "kv_hbm_frac": head["kv_hbm_frac"],
+        "stage1_us": us_s1,
+        "rounds": len(head["us_per_op_rounds"]),
+        "us_per_op_rounds": head["us_per_op_rounds"],
+        "stage1_us_rounds": head["stage1_us_rounds"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.kv_dtype == "bf16" else "f32",
         "accumulate": "f32",
@@ -296,21 +379,15 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v,
                    "page_size": w.page_size, "context": (w.context_lens[0] if len(set(w.context_lens)) == 1
                                                         else list(w.context_lens)),
-                   "num_splits": S, "rows_per_wg": plan.rows_per_wg, "head_tiles": plan.head_tiles,
-                   "stage1_waves": plan.stage1_waves, "xcd_remap": plan.xcd_remap, "plan_flags": plan.flags,
-                   "replicas": R,
+                   "num_splits": head["num_splits"], "rows_per_wg": head["rows_per_wg"],
+                   "head_tiles": head["head_tiles"], "stage1_waves": head["stage1_waves"],
+                   "xcd_remap": head["xcd_remap"], "plan_flags": head["plan_flags"], "replicas": head["replicas"],
                    "kv_bytes_per_op": kv_bytes, "parallelism": "single GPU"},
-        "tflops_per_s": round(flops / (us_op * 1e-6) / 1e12, 2),
-        "roofline": {"bound": "hbm", "kernel": "stage1", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": flops, "launch_us": round(us_s1, 3)},
+        "tflops_per_s": head["tflops_per_s"],
+        "roofline": head["roofline"],
     }
-    if compute_bound:
-        tf = flops / (us_s1 * 1e-6) / 1e12
-        res["roofline"].update({"bound": "mfma" if w.kv_dtype == "bf16" else "alu", "achieved": round(tf, 2),
-                                "peak": peak_tf, "unit": "TFLOP/s", "frac": round(tf / peak_tf, 4),
-                                "hbm_gbs": round(ach, 1)})
     if not args.no_read_probe:
+        ach = head["roofline"]["alg_bytes_per_launch"] / (us_s1 * 1e-6) / 1e9
         rp = read_probe_line(kv_bytes, args.steps, stream)
         # stage 1 against a bare read: its time relative to a cold read of
         # the same KV bytes, and its rate relative to the streaming read
@@ -319,6 +396,21 @@ def main():
         res["read_probe"] = rp
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, kv_bytes, args.cpu_seconds)
+    del inp
+    extra = [n for n in args.extra.split(",") if n and n != w.name] if args.extra else []
+    if extra:
+        res["configs"] = {}
+        for name in extra:
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            r, _ = measure(get(name), args, stream)
+            if not args.no_read_probe:
+                # a plain cold read of the same KV bytes (unique bytes where
+                # prefixes are shared), timed the same way
+                same = read_probe_same_bytes(r.get("unique_kv_bytes_per_op", r["kv_bytes_per_op"]),
+                                             args.steps, stream, res.get("read_probe", {}).get("workgroups", 4096))
+                same["same_bytes_us_over_stage1_us"] = round(same["same_bytes_cold_us"] / r["stage1_us"], 4)
+                r["read_probe"] = same
+            res["configs"][name] = r
     print(json.dumps(res), flush=True)
 
 
