@@ -45,8 +45,9 @@
  *                uint32 counter per (request, KV head, head tile) at offset 0,
  *                before o_part
  *
- * Threading and ownership: the library keeps no device memory and allocates
- * nothing; run/partials/merge only validate host-side arguments, enqueue
+ * Threading and ownership: the library allocates nothing and keeps no device
+ * memory besides the static scratch of attn_decode_run_noalloc (below);
+ * run/partials/merge only validate host-side arguments, enqueue
  * kernels on `stream` (a hipStream_t; NULL = the null stream) and return
  * without synchronising, so they may be captured into a HIP graph.  Device
  * data (page ids, context lengths) is not validated: page ids must lie in
@@ -152,7 +153,7 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
  * Full decode: stage 1 (partials into the workspace) then stage 2 (merge into
  * out and, when lse is non-null, lse), both enqueued on `stream`.  With one
  * split, stage 1 writes out and lse itself (the same bits a merge of one
- * split gives) and the workspace is not touched.
+ * split gives) and the workspace is not touched (its size is not checked).
  * num_splits = 0 uses plan->num_splits; any value in [1, plan->max_splits]
  * is allowed (results agree up to float rounding).  workspace_bytes must be
  * at least the size attn_decode_workspace_layout reports for that split
@@ -208,6 +209,31 @@ attn_status attn_decode_workspace_init(const attn_decode_plan_t* plan, void* wor
 attn_status attn_decode_split_range(const attn_decode_plan_t* plan, int32_t context_len,
                                     int32_t num_splits, int32_t split, int32_t* begin,
                                     int32_t* end);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * decode as attn_decode_run (same kernels, same bits), with the workspace
+ * taken from a static device array of ATTN_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends, instead of a
+ * caller buffer.  The caller still passes inputs and outputs.  No call
+ * allocates or frees memory; the first call on a device looks the array's
+ * address up (hipGetSymbolAddress) and keeps it, so make that first call
+ * outside graph capture.  `stream` must belong to the current device
+ * (ATTN_EINVAL otherwise).  ATTN_EWORKSPACE when more than one split is run
+ * and the split count's workspace (attn_decode_workspace_layout) exceeds
+ * the array (one split writes the output directly and needs none),
+ * ATTN_EUNSUPPORTED for plans made with ATTN_PLAN_FUSED_MERGE.  Every call
+ * on one GPU shares that GPU's array and leaves its partials there: calls
+ * that overlap in time on one GPU (other streams, other threads) race and
+ * give wrong outputs.  Nothing in the array needs to start at zero.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+attn_status attn_decode_run_noalloc(const attn_decode_plan_t* plan, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* page_table, const int32_t* context_lens,
+                                    float scale, int32_t num_splits, void* out, float* lse,
+                                    void* stream);
 
 /* Text of the calling thread's last error ("" if none).  Owned by the library;
  * valid until the thread's next failing call. */

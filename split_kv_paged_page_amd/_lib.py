@@ -26,7 +26,8 @@ ATTN_VARIANT_VALU, ATTN_VARIANT_MFMA = 1, 2
 
 EXPORTED = ["attn_decode_plan", "attn_decode_run", "attn_decode_partials", "attn_decode_merge",
             "attn_decode_workspace_layout", "attn_decode_workspace_init", "attn_decode_split_range",
-            "attn_decode_last_error"]
+            "attn_decode_run_noalloc", "attn_decode_last_error"]
+NOALLOC_SCRATCH_BYTES = 64 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
 
 _STATUS = {ATTN_OK: "ATTN_OK", ATTN_EINVAL: "ATTN_EINVAL", ATTN_EUNSUPPORTED: "ATTN_EUNSUPPORTED",
            ATTN_EWORKSPACE: "ATTN_EWORKSPACE", ATTN_EHIP: "ATTN_EHIP"}
@@ -94,6 +95,7 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_workspace_layout.argtypes = [P(AttnDecodePlan), i32, P(i64), P(i64), P(i64)]
         L.attn_decode_workspace_init.argtypes = [P(AttnDecodePlan), vp, i64, vp]
         L.attn_decode_split_range.argtypes = [P(AttnDecodePlan), i32, i32, i32, P(i32), P(i32)]
+        L.attn_decode_run_noalloc.argtypes = [P(AttnDecodePlan), vp, vp, vp, vp, vp, f32, i32, vp, vp, vp]
         L.attn_decode_last_error.argtypes = []
         L.attn_decode_last_error.restype = ctypes.c_char_p
         for n in EXPORTED[:-1]:
@@ -150,6 +152,16 @@ def attn_decode_run(plan, q, k_cache, v_cache, page_table, context_lens, scale, 
     _check(lib().attn_decode_run(ctypes.byref(plan), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                  _ptr(page_table), _ptr(context_lens), float(scale), int(num_splits),
                                  _ptr(out), _ptr(lse), _ptr(workspace), wb, _stream(stream)))
+
+
+def attn_decode_run_noalloc(plan, q, k_cache, v_cache, page_table, context_lens, scale, num_splits, out,
+                            lse, stream=None):
+    """attn_decode_run with the workspace in the library's static device
+    scratch (NOALLOC_SCRATCH_BYTES per GPU): nothing is allocated.  Calls
+    that overlap in time on one GPU race on that scratch."""
+    _check(lib().attn_decode_run_noalloc(ctypes.byref(plan), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(page_table), _ptr(context_lens), float(scale), int(num_splits),
+                                         _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def attn_decode_partials(plan, q, k_cache, v_cache, page_table, context_lens, scale, num_splits,

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "attn_decode.h"
 #include "launch.h"
@@ -145,7 +146,8 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
     return fail(ATTN_EINVAL, "scale must be positive and finite (got %g)", (double)scale);
   int64_t o_off, l_off, need;
   layout(plan, S, &o_off, &l_off, &need);
-  if (ws_bytes < need)
+  // Direct output (one split) leaves the workspace untouched.
+  if (!out && ws_bytes < need)
     return fail(ATTN_EWORKSPACE, "workspace of %lld bytes is below the %lld needed", (long long)ws_bytes,
                 (long long)need);
   splitkv::Stage1Params p{};
@@ -230,6 +232,48 @@ attn_status enqueue_stage2(const attn_decode_plan_t* plan, int S, const void* ws
   p.fd_cols = splitkv::make_fastdiv((uint32_t)(d.head_dim_v / 4));
   hipError_t e = splitkv::launch_stage2(p, d.dtype, st);
   if (e != hipSuccess) return hip_fail(e, "stage-2 launch");
+  return ATTN_OK;
+}
+
+// ---- Static scratch of the no-allocation entry point ----
+// attn_decode_run_noalloc keeps a call's workspace (the partials of every
+// split) in this device array instead of a caller buffer.  Every GPU the
+// library runs on holds its own copy from the code object's load until the
+// process ends.  In host code `scratch` names a host-side stand-in, never
+// the device memory: kernels get the address hipGetSymbolAddress returns
+// for the current device, looked up once per device and kept below.
+constexpr int64_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+// Address of this device's scratch; `stream` must belong to the current
+// device (the array's address differs from one device to the next).
+attn_status device_scratch(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (stream) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(ATTN_EINVAL, "the stream belongs to device %d but device %d is current", (int)sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_EUNSUPPORTED, "device %d is beyond the %d devices the static scratch serves", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || (uintptr_t)p % 256) return fail(ATTN_EHIP, "static scratch is not 256-byte aligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
   return ATTN_OK;
 }
 
@@ -430,6 +474,26 @@ attn_status attn_decode_run(const attn_decode_plan_t* plan, const void* q, const
                       workspace_bytes, (hipStream_t)stream);
   if (st != ATTN_OK) return st;
   return enqueue_stage2(plan, S, workspace, workspace_bytes, out, lse, (hipStream_t)stream);
+}
+
+attn_status attn_decode_run_noalloc(const attn_decode_plan_t* plan, const void* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* page_table, const int32_t* context_lens,
+                                    float scale, int32_t num_splits, void* out, float* lse, void* stream) {
+  int S;
+  attn_status st = resolve_splits(plan, num_splits, &S);
+  if (st != ATTN_OK) return st;
+  if (plan->flags & ATTN_PLAN_FUSED_MERGE)
+    return fail(ATTN_EUNSUPPORTED, "the no-allocation call does not take ATTN_PLAN_FUSED_MERGE plans");
+  int64_t need;
+  layout(plan, S, nullptr, nullptr, &need);
+  if (S > 1 && need > kScratchBytes)   // one split writes the output directly, no partials
+    return fail(ATTN_EWORKSPACE, "%d splits need a %lld-byte workspace, above the %lld-byte static scratch", S,
+                (long long)need, (long long)kScratchBytes);
+  void* ws = nullptr;
+  st = device_scratch((hipStream_t)stream, &ws);
+  if (st != ATTN_OK) return st;
+  return attn_decode_run(plan, q, k_cache, v_cache, page_table, context_lens, scale, S, out, lse, ws,
+                         kScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -293,6 +293,39 @@ def test_run_argument_errors_before_any_launch():
             assert ei.value.status == sk.ATTN_EINVAL, bad
 
 
+def test_noalloc_rejects_plans_beyond_its_scratch_before_any_hip_call():
+    """The no-allocation entry point checks the plan's workspace against its
+    static scratch, and the plan flags, before it touches the HIP runtime."""
+    fake = 1 << 20
+    mla = desc(B=64, Hq=128, Hkv=1, Dk=576, Dv=512, P=1, maxp=16384, alias=1, pages=1 << 20)
+    big = sk.attn_decode_plan(mla, 16384, 8, 0)           # 8 splits: 268 MB of partials
+    assert sk.attn_decode_workspace_layout(big, 8)[2] > sk.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_run_noalloc(big, fake, fake, fake, fake, fake, 0.04, 8, fake, None, stream=0)
+    assert ei.value.status == sk.ATTN_EWORKSPACE
+    assert "static scratch" in sk.attn_decode_last_error()
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_run_noalloc(big, fake, fake, fake, fake, fake, 0.04, 9, fake, None, stream=0)
+    assert ei.value.status == sk.ATTN_EWORKSPACE             # beyond the plan's max_splits
+    fused = sk.attn_decode_plan(mla, 16384, 2, sk.ATTN_PLAN_FUSED_MERGE)
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_run_noalloc(fused, fake, fake, fake, fake, fake, 0.04, 2, fake, None, stream=0)
+    assert ei.value.status == sk.ATTN_EUNSUPPORTED
+    # every full-size workload's default plan fits the scratch
+    from workloads import CONFIGS
+    for w in CONFIGS.values():
+        ks = (w.num_kv_heads * w.page_size * w.head_dim_qk, w.page_size * w.head_dim_qk, w.head_dim_qk)
+        vs = ks if w.v_aliases_k else (w.num_kv_heads * w.page_size * w.head_dim_v, w.page_size * w.head_dim_v,
+                                       w.head_dim_v)
+        d = sk.make_desc(batch=w.batch, q_len=w.q_len, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                         head_dim_qk=w.head_dim_qk, head_dim_v=w.head_dim_v, page_size=w.page_size,
+                         max_pages_per_req=w.max_pages_per_req,
+                         dtype=sk.ATTN_F32 if w.kv_dtype == "f32" else sk.ATTN_BF16, causal=int(w.causal),
+                         v_aliases_k=int(w.v_aliases_k), num_pages=w.pool_pages, k_strides=ks, v_strides=vs)
+        p = sk.attn_decode_plan(d, max(w.context_lens), w.num_splits, 0)
+        assert p.num_splits == 1 or p.workspace_bytes <= sk.NOALLOC_SCRATCH_BYTES, w.name
+
+
 def test_xcd_order_only_for_batched_single_position_decode():
     """The split-major XCD-contiguous order is planned for decode batches
     (requests that may share KV on one XCD's L2), not for one request and not
