@@ -29,7 +29,9 @@ Readings where the pages are silent:
 * key t of request b lives at page_table[b][t // P], slot t % P;
 * split s of S covers [s*c, min((s+1)*c, L)) with c = A * ceil(ceil(L/S)/A),
   A = 64 keys (the 64-key block the trip counts in the aiter PR's tables
-  imply); a split with no visible key gives out = 0, lse = -inf;
+  imply), or with c a fixed split length shared by every request of a
+  batch (a request then holds ceil(L/c) non-empty splits); a split with no
+  visible key gives out = 0, lse = -inf;
 * an empty row (no visible key) gives out = 0, lse = -inf.
 """
 
@@ -66,16 +68,27 @@ def visible_keys(L: int, q_len: int, j: int, causal: bool) -> int:
     return max(0, L - q_len + 1 + j)
 
 
-def split_bounds(L: int, S: int, A: int = SPLIT_ALIGN) -> list:
+def split_bounds(L: int, S: int, A: int = SPLIT_ALIGN, chunk: int | None = None) -> list:
     """[begin, end) of each of the S splits of a request with L keys.
 
     Every split but the last holds the same whole number of A-key blocks; the
     trip count per stage-1 program is then ceil(L / S / A) as in the aiter
     PR's Test Result tables.
+
+    With ``chunk`` given, every request of a batch cuts its keys into splits
+    of that fixed length instead: split s covers [s*chunk, min((s+1)*chunk,
+    L)), so a request holds ceil(L / chunk) non-empty splits, in proportion
+    to its length, and the splits past them are empty.  (The pages trade the
+    split count against each program's walk length; with mixed lengths a
+    fixed walk length per split keeps every program's walk equal.)
     """
     if S < 1 or A < 1:
         raise ValueError("S and A must be positive")
-    chunk = A * (-(-(-(-L // S)) // A)) if L > 0 else A
+    if chunk is not None:
+        if chunk < 1:
+            raise ValueError("chunk must be positive")
+    else:
+        chunk = A * (-(-(-(-L // S)) // A)) if L > 0 else A
     out = []
     for s in range(S):
         b = min(s * chunk, max(L, 0))
@@ -179,8 +192,9 @@ def decode_reference(inp, requests=None) -> tuple:
     return out, lse
 
 
-def split_reference(inp, S: int, A: int = SPLIT_ALIGN, requests=None) -> tuple:
-    """Per-split normalised partial outputs and log-sum-exps.
+def split_reference(inp, S: int, A: int = SPLIT_ALIGN, requests=None, chunk: int | None = None) -> tuple:
+    """Per-split normalised partial outputs and log-sum-exps, splits as in
+    split_bounds (``chunk``: fixed split length for every request).
 
     Returns (o_part [B, q_len, H_q, S, Dv], lse_part [B, q_len, H_q, S]).
     """
@@ -190,7 +204,7 @@ def split_reference(inp, S: int, A: int = SPLIT_ALIGN, requests=None) -> tuple:
     lse_part = np.full((w.batch, w.q_len, w.num_q_heads, S), np.nan)
     for b in (range(w.batch) if requests is None else requests):
         L = int(inp.context_lens[b])
-        bounds = split_bounds(L, S, A)
+        bounds = split_bounds(L, S, A, chunk)
         for kvh in range(w.num_kv_heads):
             idx, qr = _request_rows(inp, b, kvh)
             K, V = _kv(inp, b, kvh, L)

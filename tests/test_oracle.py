@@ -308,6 +308,48 @@ def test_split_rule_bruteforce():
                 assert covered == list(range(L))
 
 
+def test_fixed_chunk_split_rule_bruteforce():
+    """Fixed split length c for every request: the S splits partition the
+    first min(L, S*c) keys in order, each non-empty split but the last of a
+    request holds exactly c keys, the request holds ceil(L / c) non-empty
+    splits, and every later split is empty (begin = end = the end of the
+    keys)."""
+    for L in range(0, 200):
+        for c in (1, 2, 3, 16, 64, 128):
+            for S in sorted({1, 2, 5, max(1, -(-L // c)), max(1, -(-L // c)) + 3}):
+                bounds = oracle.split_bounds(L, S, 64, chunk=c)
+                assert len(bounds) == S
+                covered = [t for b, e in bounds for t in range(b, e)]
+                assert covered == list(range(min(L, S * c))), (L, c, S)
+                lens = [e - b for b, e in bounds]
+                live = [n for n in lens if n > 0]
+                assert len(live) == min(S, -(-L // c)), (L, c, S)
+                assert all(n == c for n in live[:-1])
+                first_empty = len(live)
+                assert all(n == 0 for n in lens[first_empty:])
+                assert all(b == e == min(L, S * c) for b, e in bounds[first_empty:])
+
+
+def test_fixed_chunk_split_merge_reproduces_unsplit():
+    # per-request split counts in proportion to length (ragged batch, causal
+    # drafts): the merged partials equal the unsplit result whenever S * c
+    # covers the longest request
+    for case in (CASES[3], CASES[4], dict(B=3, Hq=8, Hkv=2, Dk=32, Dv=32, P=1, ctx=(1, 7, 20))):
+        w = _wl(**case)
+        inp, *_ = dense_problem(w, seed=13)
+        o, l = oracle.decode_reference(inp)
+        for c in (1, 2, 4, 7):
+            S = -(-max(w.context_lens) // c)
+            op, lp = oracle.split_reference(inp, S, chunk=c)
+            mo, ml = oracle.merge_reference(op, lp)
+            assert np.max(np.abs(mo - o)) <= 1e-12 and np.max(np.abs(ml - l)) <= 1e-12, (case, c)
+            # a split count that stops short of the longest request loses keys
+            if S > 1:
+                op2, lp2 = oracle.split_reference(inp, S - 1, chunk=c)
+                mo2, _ = oracle.merge_reference(op2, lp2)
+                assert np.max(np.abs(mo2 - o)) > 1e-6
+
+
 def test_visible_keys_rule():
     assert oracle.visible_keys(10, 1, 0, True) == 10
     assert [oracle.visible_keys(10, 4, j, True) for j in range(4)] == [7, 8, 9, 10]
