@@ -251,7 +251,9 @@ def measure(w, args, stream, splits=0, flags=0, want_inputs=False):
     t = upload(inp, "cuda")
     desc = sk.make_desc_from_tensors(t["q"], t["k_cache"], t["v_cache"], t["page_table"],
                                      head_dim_v=w.head_dim_v, causal=w.causal)
-    plan = sk.attn_decode_plan(desc, int(max(w.context_lens)), splits or w.num_splits, flags)
+    # the workload's lengths are known on the host (ragged batches may get
+    # one fixed split length for every request)
+    plan = sk.attn_decode_plan_lens(desc, [int(x) for x in w.context_lens], splits or w.num_splits, flags)
     S = plan.num_splits
     kv_bytes, alg_bytes = algorithmic_bytes(w, S)
     touched = w.unique_kv_bytes()
@@ -273,6 +275,11 @@ def measure(w, args, stream, splits=0, flags=0, want_inputs=False):
 
     def stage1(i):
         r = i % R
+        if S == 1:
+            # one split: the op is stage 1 alone, writing the output itself
+            # (the partials call would write fp32 partials instead)
+            step(i)
+            return
         sk.attn_decode_partials(plan, t["q"], ks[r], vs[r], t["page_table"], t["context_lens"], scale, S,
                                 ws, stream=stream.cuda_stream)
 
@@ -317,7 +324,8 @@ def measure(w, args, stream, splits=0, flags=0, want_inputs=False):
         "us_per_op_rounds": [round(x * 1e3 / args.steps, 3) for x in op_rounds],
         "stage1_us_rounds": [round(x * 1e3 / args.steps, 3) for x in s1_rounds],
         "tflops_per_s": round(flops / (us_op * 1e-6) / 1e12, 2),
-        "num_splits": S, "rows_per_wg": plan.rows_per_wg, "head_tiles": plan.head_tiles,
+        "num_splits": S, "split_chunk": plan.split_chunk, "rows_per_wg": plan.rows_per_wg,
+        "head_tiles": plan.head_tiles,
         "stage1_waves": plan.stage1_waves, "xcd_remap": plan.xcd_remap, "plan_flags": plan.flags,
         "replicas": R, "kv_bytes_per_op": kv_bytes,
         "roofline": {"bound": "hbm", "kernel": "stage1", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
@@ -379,7 +387,8 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v,
                    "page_size": w.page_size, "context": (w.context_lens[0] if len(set(w.context_lens)) == 1
                                                         else list(w.context_lens)),
-                   "num_splits": head["num_splits"], "rows_per_wg": head["rows_per_wg"],
+                   "num_splits": head["num_splits"], "split_chunk": head["split_chunk"],
+                   "rows_per_wg": head["rows_per_wg"],
                    "head_tiles": head["head_tiles"], "stage1_waves": head["stage1_waves"],
                    "xcd_remap": head["xcd_remap"], "plan_flags": head["plan_flags"], "replicas": head["replicas"],
                    "kv_bytes_per_op": kv_bytes, "parallelism": "single GPU"},

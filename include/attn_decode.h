@@ -24,7 +24,12 @@
  * Split rule (host and device agree; attn_decode_split_range exposes it):
  * chunk = A * ceil(ceil(ctx / S) / A) with A = split_align (64 keys); split s
  * covers [s*chunk, min((s+1)*chunk, ctx)).  The 64-key block is the block
- * the trip counts of the aiter PR's Test Result tables imply.
+ * the trip counts of the aiter PR's Test Result tables imply.  A plan with
+ * split_chunk > 0 (attn_decode_plan_lens) uses chunk = split_chunk for every
+ * request instead, and request b has n_b = ceil(host_len[b] / chunk) splits
+ * (plan->split_start), so requests hold splits in proportion to their
+ * lengths; its partials fill slots 0 .. n_b - 1 of the S (= plan->num_splits,
+ * the largest n_b) slots per row, and the merge reads those slots only.
  *
  * Memory layouts (all device memory, caller-owned, element strides):
  *   q            [B, q_len, H_q, Dk]  contiguous, dtype
@@ -103,6 +108,9 @@ enum {
                                        256/256, 576/512 with V = K[:512]) */
 };
 
+/* Requests a plan's split table covers (attn_decode_plan_lens). */
+#define ATTN_MAX_SPLIT_TABLE 64
+
 /* Shape and layout of one decode call; filled by the caller. */
 typedef struct attn_decode_desc {
   int32_t batch;              /* B >= 1 requests */
@@ -135,8 +143,16 @@ typedef struct attn_decode_plan_t {
   int32_t stage1_waves;       /* wavefronts per stage-1 workgroup */
   int32_t xcd_remap;          /* 1: split-major, XCD-contiguous workgroup order */
   int32_t flags;              /* ATTN_PLAN_* given to attn_decode_plan */
+  int32_t split_chunk;        /* > 0: fixed split length in keys for every request (plans from
+                                 attn_decode_plan_lens); 0: the split-count rule */
+  int32_t live_splits;        /* with split_chunk > 0: stage-1 work items (request, split) in all,
+                                 split_start[batch]; 0 otherwise */
   int64_t workspace_bytes;    /* bytes the caller must provide at max_splits */
   uint64_t key;               /* hash of every field a kernel specialisation depends on */
+  int32_t split_start[ATTN_MAX_SPLIT_TABLE + 1];
+                              /* with split_chunk > 0: request b owns work items
+                                 [split_start[b], split_start[b+1]), its splits 0 .. n_b - 1 with
+                                 n_b = ceil(host_context_lens[b] / split_chunk); unused entries 0 */
 } attn_decode_plan_t;
 
 /*
@@ -148,6 +164,29 @@ typedef struct attn_decode_plan_t {
  */
 attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_len,
                              int32_t num_splits, int32_t flags, attn_decode_plan_t* plan);
+
+/*
+ * Plan a decode call whose context lengths are known on the host:
+ * host_context_lens holds `batch` lengths (host memory, read during the call
+ * only).  Same as attn_decode_plan with max_context_len = their maximum,
+ * except that the split policy (num_splits = 0, no ATTN_PLAN_POLICY_P2 or
+ * ATTN_PLAN_FUSED_MERGE, batch <= ATTN_MAX_SPLIT_TABLE) may give every
+ * request the same split length (plan->split_chunk keys, a multiple of 64)
+ * instead of the same split count: request b then gets n_b =
+ * ceil(host_context_lens[b] / split_chunk) splits, in proportion to its
+ * length, and stage 1 runs one workgroup per (request, split) pair of that
+ * flat work list (plan->split_start), so every workgroup walks about the
+ * same number of keys and no workgroup is launched for a split that holds
+ * none (aiter PR #4758, Motivation: the split count trades parallelism
+ * against walk length).  It does so when that shortens the longest walk
+ * while the work list still fits one round of workgroups on the 256 CUs.
+ * Such a plan runs with its own split count (num_splits 0 or
+ * plan->num_splits, ATTN_EINVAL otherwise).  Precondition for such a plan:
+ * each device context_lens[b] <= host_context_lens[b] (a shorter one leaves
+ * some of its splits empty; keys past n_b * split_chunk would be ignored).
+ */
+attn_status attn_decode_plan_lens(const attn_decode_desc* desc, const int32_t* host_context_lens,
+                                  int32_t num_splits, int32_t flags, attn_decode_plan_t* plan);
 
 /*
  * Full decode: stage 1 (partials into the workspace) then stage 2 (merge into
@@ -170,7 +209,8 @@ attn_status attn_decode_run(const attn_decode_plan_t* plan, const void* q,
                             void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Stage 1 only: writes o_part / lse_part of every split into the workspace
- * (an empty split writes zeros and -inf).  Same arguments as run. */
+ * (an empty split writes zeros and -inf; with a split table, request b's
+ * slots n_b .. S - 1 are left untouched).  Same arguments as run. */
 attn_status attn_decode_partials(const attn_decode_plan_t* plan, const void* q,
                                  const void* k_cache, const void* v_cache,
                                  const int32_t* page_table, const int32_t* context_lens,

@@ -24,10 +24,11 @@ ATTN_PLAN_NO_XCD_REMAP = 2
 ATTN_PLAN_FUSED_MERGE = 4
 ATTN_VARIANT_VALU, ATTN_VARIANT_MFMA = 1, 2
 
-EXPORTED = ["attn_decode_plan", "attn_decode_run", "attn_decode_partials", "attn_decode_merge",
+EXPORTED = ["attn_decode_plan", "attn_decode_plan_lens", "attn_decode_run", "attn_decode_partials", "attn_decode_merge",
             "attn_decode_workspace_layout", "attn_decode_workspace_init", "attn_decode_split_range",
             "attn_decode_run_noalloc", "attn_decode_last_error"]
 NOALLOC_SCRATCH_BYTES = 64 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
+MAX_SPLIT_TABLE = 64               # ATTN_MAX_SPLIT_TABLE
 
 _STATUS = {ATTN_OK: "ATTN_OK", ATTN_EINVAL: "ATTN_EINVAL", ATTN_EUNSUPPORTED: "ATTN_EUNSUPPORTED",
            ATTN_EWORKSPACE: "ATTN_EWORKSPACE", ATTN_EHIP: "ATTN_EHIP"}
@@ -51,11 +52,13 @@ class AttnDecodeDesc(ctypes.Structure):
 class AttnDecodePlan(ctypes.Structure):
     _fields_ = [("desc", AttnDecodeDesc)] + [(n, ctypes.c_int32) for n in (
         "max_context_len", "num_splits", "max_splits", "split_align", "variant", "rows_per_wg",
-        "head_tiles", "stage1_waves", "xcd_remap", "flags")] + \
-        [("workspace_bytes", ctypes.c_int64), ("key", ctypes.c_uint64)]
+        "head_tiles", "stage1_waves", "xcd_remap", "flags", "split_chunk", "live_splits")] + \
+        [("workspace_bytes", ctypes.c_int64), ("key", ctypes.c_uint64),
+         ("split_start", ctypes.c_int32 * (MAX_SPLIT_TABLE + 1))]
 
     def as_dict(self) -> dict:
-        d = {f: getattr(self, f) for f, _ in self._fields_ if f != "desc"}
+        d = {f: getattr(self, f) for f, _ in self._fields_ if f not in ("desc", "split_start")}
+        d["split_start"] = list(self.split_start)
         d["desc"] = {f: getattr(self.desc, f) for f, _ in AttnDecodeDesc._fields_}
         return d
 
@@ -89,6 +92,7 @@ def lib() -> ctypes.CDLL:
         P = ctypes.POINTER
         vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         L.attn_decode_plan.argtypes = [P(AttnDecodeDesc), i32, i32, i32, P(AttnDecodePlan)]
+        L.attn_decode_plan_lens.argtypes = [P(AttnDecodeDesc), P(i32), i32, i32, P(AttnDecodePlan)]
         L.attn_decode_run.argtypes = [P(AttnDecodePlan), vp, vp, vp, vp, vp, f32, i32, vp, vp, vp, i64, vp]
         L.attn_decode_partials.argtypes = [P(AttnDecodePlan), vp, vp, vp, vp, vp, f32, i32, vp, i64, vp]
         L.attn_decode_merge.argtypes = [P(AttnDecodePlan), i32, vp, i64, vp, vp, vp]
@@ -143,6 +147,19 @@ def attn_decode_plan(desc: AttnDecodeDesc, max_context_len: int, num_splits: int
                      flags: int = 0) -> AttnDecodePlan:
     p = AttnDecodePlan()
     _check(lib().attn_decode_plan(ctypes.byref(desc), max_context_len, num_splits, flags, ctypes.byref(p)))
+    return p
+
+
+def attn_decode_plan_lens(desc: AttnDecodeDesc, host_context_lens, num_splits: int = 0,
+                          flags: int = 0) -> AttnDecodePlan:
+    """Plan with the batch's context lengths known on the host (a sequence of
+    ints); the policy may then fix one split length for every request."""
+    lens = [int(x) for x in host_context_lens]
+    if len(lens) != desc.batch:
+        raise ValueError(f"{len(lens)} context lengths for a batch of {desc.batch}")
+    arr = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+    p = AttnDecodePlan()
+    _check(lib().attn_decode_plan_lens(ctypes.byref(desc), arr, num_splits, flags, ctypes.byref(p)))
     return p
 
 

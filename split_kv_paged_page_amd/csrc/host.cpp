@@ -125,6 +125,11 @@ attn_status resolve_splits(const attn_decode_plan_t* p, int32_t num_splits, int*
   *S = num_splits ? num_splits : p->num_splits;
   if (*S > p->max_splits)
     return fail(ATTN_EWORKSPACE, "num_splits %d exceeds the plan's max_splits %d", *S, p->max_splits);
+  // With a fixed split length the plan's split count is the one that covers
+  // its longest request; fewer would leave keys out.
+  if (p->split_chunk > 0 && *S != p->num_splits)
+    return fail(ATTN_EINVAL, "a plan with %d-key splits runs with its own %d splits (got %d)", p->split_chunk,
+                p->num_splits, *S);
   return ATTN_OK;
 }
 
@@ -178,6 +183,10 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   p.causal = d.causal;
   p.num_splits = S;
   p.split_align = plan->split_align;
+  p.split_chunk = plan->split_chunk;
+  p.live_splits = plan->live_splits;
+  for (int i = 0; i <= ATTN_MAX_SPLIT_TABLE; ++i) p.split_start[i] = plan->split_start[i];
+  p.fd_live = splitkv::make_fastdiv((uint32_t)(plan->live_splits > 0 ? plan->live_splits : 1));
   p.align_shift = 0;
   while ((1 << p.align_shift) < p.split_align) ++p.align_shift;
   p.fd_tiles = splitkv::make_fastdiv((uint32_t)plan->head_tiles);
@@ -187,12 +196,16 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   p.fd_group = splitkv::make_fastdiv((uint32_t)(d.num_q_heads / d.num_kv_heads));
   p.rows_total = p.group * d.q_len;
   // One request: its context is most likely the longest the plan was made
-  // for.  Batches mix lengths, and a wrong guess costs more than it saves.
-  p.guess_ctx = d.batch == 1 ? plan->max_context_len : 0;
+  // for.  Batches mix lengths, and a wrong guess costs more than it saves,
+  // except under a split table: there a workgroup knows its split's start
+  // without the context length, and its end whenever the split is not its
+  // request's last (the kernels then guess min((s + 1) * chunk, max)).
+  p.guess_ctx = d.batch == 1 || plan->live_splits > 0 ? plan->max_context_len : 0;
   p.rows_per_wg = plan->rows_per_wg;
   p.head_tiles = plan->head_tiles;
   p.xcd_remap = plan->xcd_remap;
-  const int64_t nwg = (int64_t)S * d.batch * d.num_kv_heads * plan->head_tiles;
+  const int64_t nwg = (int64_t)(plan->live_splits > 0 ? plan->live_splits : (int64_t)S * d.batch) *
+                     d.num_kv_heads * plan->head_tiles;
   if (nwg > 0x7fffffff) return fail(ATTN_EINVAL, "grid too large");
   p.num_wgs = (int32_t)nwg;
   p.ks_page = d.k_stride_page;
@@ -230,6 +243,9 @@ attn_status enqueue_stage2(const attn_decode_plan_t* plan, int S, const void* ws
   p.num_splits = S;
   p.head_dim_v = d.head_dim_v;
   p.fd_cols = splitkv::make_fastdiv((uint32_t)(d.head_dim_v / 4));
+  p.live_splits = plan->live_splits;
+  for (int i = 0; i <= ATTN_MAX_SPLIT_TABLE; ++i) p.split_start[i] = plan->split_start[i];
+  p.fd_req_rows = splitkv::make_fastdiv((uint32_t)(d.q_len * d.num_q_heads));
   hipError_t e = splitkv::launch_stage2(p, d.dtype, st);
   if (e != hipSuccess) return hip_fail(e, "stage-2 launch");
   return ATTN_OK;
@@ -283,8 +299,14 @@ extern "C" {
 
 const char* attn_decode_last_error(void) { return g_err; }
 
-attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_len, int32_t num_splits,
-                             int32_t flags, attn_decode_plan_t* plan) {
+}  // extern "C"
+
+namespace {
+
+// The planner behind attn_decode_plan and attn_decode_plan_lens; `lens`
+// (batch entries, host memory) may be null.
+attn_status plan_impl(const attn_decode_desc* desc, int32_t max_context_len, const int32_t* lens,
+                      int32_t num_splits, int32_t flags, attn_decode_plan_t* plan) {
   if (!plan) return fail(ATTN_EINVAL, "plan is null");
   attn_status st = check_desc(desc);
   if (st != ATTN_OK) return st;
@@ -368,10 +390,43 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
     // context (the split rule rounds chunks up to 64 keys): they cost partial
     // writes and merge reads and change no chunk.  Drafts (longest 2,048 keys,
     // 10 -> 8 splits): 16.6 -> 16.3 us per op.
+    int64_t chunk_u = kSplitAlign;   // the longest split walk under the split-count rule
     if (max_context_len > 0) {
       const int64_t per = (max_context_len + (int64_t)S - 1) / S;
-      const int64_t chunk = (per + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
-      S = (int)((max_context_len + chunk - 1) / chunk);
+      chunk_u = (per + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+      S = (int)((max_context_len + chunk_u - 1) / chunk_u);
+    }
+    // Known lengths (attn_decode_plan_lens): one split length for every
+    // request, so that each request holds splits in proportion to its
+    // length and every workgroup walks about the same number of keys.  The
+    // shortest multiple of 64 keys whose live workgroups still fit one
+    // round is taken when it shortens the longest walk of the rule above,
+    // which gives every request the same split count.  Drafts (lengths 256
+    // to 2,048): 64-key splits would need 384 workgroups; 128-key splits
+    // need 192 and walk 128 keys where the split-count rule walks 256.
+    // The work list holds one stage-1 workgroup per (request, split), so
+    // no workgroup is launched for a split without keys (with one split
+    // count for all, the short requests' empty splits each held a CU while
+    // they wrote their zero partials, and delayed the long requests' late
+    // splits).
+    if (lens && max_context_len > 0 && d.batch <= ATTN_MAX_SPLIT_TABLE && !(flags & ATTN_PLAN_FUSED_MERGE)) {
+      const int64_t per_req = (int64_t)d.num_kv_heads * p.head_tiles;
+      for (int64_t c = kSplitAlign; c < chunk_u; c += kSplitAlign) {
+        int64_t live = 0;
+        for (int b = 0; b < d.batch; ++b) live += (lens[b] + c - 1) / c;
+        if (live * per_req <= target && (max_context_len + c - 1) / c <= kMaxSplits) {
+          p.split_chunk = (int32_t)c;
+          S = (int)((max_context_len + c - 1) / c);
+          int32_t at = 0;
+          for (int b = 0; b < d.batch; ++b) {
+            p.split_start[b] = at;
+            at += (int32_t)((lens[b] + c - 1) / c);
+          }
+          p.split_start[d.batch] = at;
+          p.live_splits = at;
+          break;
+        }
+      }
     }
   }
   if (S > kMaxSplits) S = kMaxSplits;
@@ -387,12 +442,36 @@ attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_l
   // missed the batch baked into the binary).
   uint64_t h = fnv1a(&p.desc, sizeof(p.desc));
   const int32_t fields[] = {p.max_context_len, p.num_splits, p.max_splits, p.split_align, p.variant,
-                            p.rows_per_wg,     p.head_tiles, p.stage1_waves, p.xcd_remap, p.flags};
+                            p.rows_per_wg,     p.head_tiles, p.stage1_waves, p.xcd_remap, p.flags,
+                            p.split_chunk, p.live_splits};
   h = fnv1a(fields, sizeof(fields), h);
+  h = fnv1a(p.split_start, sizeof(p.split_start), h);
   p.key = h;
   *plan = p;
   g_err[0] = 0;
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_decode_plan(const attn_decode_desc* desc, int32_t max_context_len, int32_t num_splits,
+                             int32_t flags, attn_decode_plan_t* plan) {
+  return plan_impl(desc, max_context_len, nullptr, num_splits, flags, plan);
+}
+
+attn_status attn_decode_plan_lens(const attn_decode_desc* desc, const int32_t* host_context_lens,
+                                  int32_t num_splits, int32_t flags, attn_decode_plan_t* plan) {
+  if (!desc) return fail(ATTN_EINVAL, "desc is null");
+  if (!host_context_lens) return fail(ATTN_EINVAL, "host_context_lens is null");
+  if (desc->batch < 1) return fail(ATTN_EINVAL, "batch, q_len and head counts must be >= 1");
+  int32_t mx = 0;
+  for (int b = 0; b < desc->batch; ++b) {
+    if (host_context_lens[b] < 0) return fail(ATTN_EINVAL, "host_context_lens[%d] is negative", b);
+    if (host_context_lens[b] > mx) mx = host_context_lens[b];
+  }
+  return plan_impl(desc, mx, host_context_lens, num_splits, flags, plan);
 }
 
 attn_status attn_decode_workspace_layout(const attn_decode_plan_t* plan, int32_t num_splits,
@@ -426,10 +505,14 @@ attn_status attn_decode_split_range(const attn_decode_plan_t* plan, int32_t cont
   const int S = num_splits ? num_splits : plan->num_splits;
   if (context_len < 0) return fail(ATTN_EINVAL, "context_len must be >= 0");
   if (split < 0 || split >= S) return fail(ATTN_EINVAL, "split %d outside [0, %d)", split, S);
+  if (plan->split_chunk > 0 && S != plan->num_splits)
+    return fail(ATTN_EINVAL, "a plan with %d-key splits has %d splits (got %d)", plan->split_chunk,
+                plan->num_splits, S);
   const int64_t A = plan->split_align;
   const int64_t per = (context_len + (int64_t)S - 1) / S;
   int64_t chunk = (per + A - 1) / A * A;
   if (chunk <= 0) chunk = A;
+  if (plan->split_chunk > 0) chunk = plan->split_chunk;
   const int64_t b = (int64_t)split * chunk, e = b + chunk;
   *begin = (int32_t)(b < context_len ? b : context_len);
   *end = (int32_t)(e < context_len ? e : context_len);

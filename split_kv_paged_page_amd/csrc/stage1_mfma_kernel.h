@@ -177,10 +177,9 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   auto tile_k = [&](int buf) { return smem + (kw * C::NBUF + buf) * C::TILE; };
   auto tile_v = [&](int buf) { return VALIAS ? tile_k(buf) : tile_k(buf) + C::KTILE; };
 
+  read_stage1_start_args(p);
   const uint32_t lid = (uint32_t)logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap);
-  const WgCoord wc = p.causal ? wg_coord_tiles_last(lid, p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch, p.fd_splits,
-                                                    p.num_splits)
-                              : wg_coord(lid, p.fd_tiles, p.head_tiles, p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch);
+  const WgCoord wc = stage1_coord(p, lid);
   // Causal rows: later head tiles hold later query positions, which see more
   // keys, so they are handed out first (longest work first; the numbering
   // is a relabelling and changes no result).
@@ -195,7 +194,7 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   // Split bounds [sb_, se_) for context length Lc, and the workgroup's last
   // visible key in the split (emax_, at least sb_).
   auto bounds = [&](int Lc, int& sb_, int& se_, int& emax_) {
-    split_range(Lc, p.num_splits, p.fd_splits, p.align_shift, s, sb_, se_);
+    split_range(Lc, p.num_splits, p.fd_splits, p.align_shift, p.split_chunk, s, sb_, se_);
     const int j = (int)fdiv((uint32_t)last_row, p.fd_group);
     const int nv = p.causal ? Lc - p.q_len + 1 + j : Lc;
     emax_ = nv < se_ ? nv : se_;
@@ -223,7 +222,11 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
   // and a second request.  That takes one dependent load off the start.
   int sb_g = 0, se_g = 0, em_g = 0;
   if constexpr (NB > 1) {
-    if (p.guess_ctx > 0) bounds(p.guess_ctx, sb_g, se_g, em_g);
+    // Under a split table the split starts at s * chunk whatever the length,
+    // and ends at (s + 1) * chunk unless it is its request's last.
+    int gctx = p.guess_ctx;
+    if (p.live_splits > 0 && (s + 1) * p.split_chunk < gctx) gctx = (s + 1) * p.split_chunk;
+    if (gctx > 0) bounds(gctx, sb_g, se_g, em_g);
     if (em_g > sb_g) {
 #pragma unroll
       for (int j = 0; j < D; ++j) issue_pid_at(sb_g, em_g, j, j);

@@ -74,10 +74,9 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
   const int x = lane & 15;
   uint8_t* wave_lds = smem + C::QB + wave * C::WAVE_B;
 
+  read_stage1_start_args(p);
   const uint32_t lid = (uint32_t)logical_wg(blockIdx.x, p.num_wgs, p.xcd_remap);
-  const WgCoord wc = p.causal ? wg_coord_tiles_last(lid, p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch, p.fd_splits,
-                                                    p.num_splits)
-                              : wg_coord(lid, p.fd_tiles, p.head_tiles, p.fd_kvh, p.num_kv_heads, p.fd_batch, p.batch);
+  const WgCoord wc = stage1_coord(p, lid);
   // Causal rows: later head tiles hold later query positions, which see more
   // keys, so they are handed out first (longest work first; the numbering
   // is a relabelling and changes no result).
@@ -86,7 +85,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
 
   const int L = p.ctx[b];
   int sb, se;
-  split_range(L, p.num_splits, p.fd_splits, p.align_shift, s, sb, se);
+  split_range(L, p.num_splits, p.fd_splits, p.align_shift, p.split_chunk, s, sb, se);
 
   int row_end[RT];
   int end_max = sb;

@@ -51,6 +51,17 @@ __device__ __forceinline__ float lanes_sum(float x) {
 
 template <int DTYPE, int LP>
 __global__ __launch_bounds__(64) void stage2_kernel(Stage2Params p) {
+  // Every argument read in one round at entry (the empty statements only
+  // hold the values in scalar registers), instead of a chain of reads after
+  // branches on earlier ones.
+  asm volatile("" ::"s"(p.rows), "s"(p.num_splits), "s"(p.head_dim_v), "s"(p.live_splits), "s"(p.fd_cols.mul),
+               "s"(p.fd_cols.shift), "s"(p.fd_req_rows.mul), "s"(p.fd_req_rows.shift), "s"(p.o_part),
+               "s"(p.lse_part), "s"(p.out), "s"(p.lse));
+  asm volatile("" ::"s"(p.split_start[0]), "s"(p.split_start[1]), "s"(p.split_start[2]), "s"(p.split_start[3]),
+               "s"(p.split_start[4]), "s"(p.split_start[5]), "s"(p.split_start[6]), "s"(p.split_start[7]),
+               "s"(p.split_start[8]), "s"(p.split_start[9]), "s"(p.split_start[10]), "s"(p.split_start[11]),
+               "s"(p.split_start[12]), "s"(p.split_start[13]), "s"(p.split_start[14]), "s"(p.split_start[15]),
+               "s"(p.split_start[16]));
   const int Dv = p.head_dim_v;
   const int cols = Dv / 4;
   const int sl = threadIdx.x & (LP - 1);
@@ -60,9 +71,16 @@ __global__ __launch_bounds__(64) void stage2_kernel(Stage2Params p) {
   if ((int)rq >= p.rows) return;   // the LP lanes of a pair leave together
   const int64_t row = rq;
   const int c = (int)(pair - rq * cols);
-  const int S = p.num_splits;
-  const float* lse_row = p.lse_part + row * S;
-  const float* base = p.o_part + row * S * Dv + c * 4;
+  const int SS = p.num_splits;   // slots per row
+  // Splits this row merges: all slots, or under a split table its
+  // request's count (the later slots are not written).
+  int S = SS;
+  if (p.live_splits > 0) {
+    const int b = (int)fdiv(rq, p.fd_req_rows);
+    S = table_entry(p.split_start, b + 1) - table_entry(p.split_start, b);
+  }
+  const float* lse_row = p.lse_part + row * SS;
+  const float* base = p.o_part + row * SS * Dv + c * 4;
 
   float ls[kPer];
   float4 ov[kPer];

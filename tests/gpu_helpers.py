@@ -32,7 +32,8 @@ def validate_inputs(inp):
 class Decode:
     """One uploaded problem + plan; run() calls attn_decode_run."""
 
-    def __init__(self, inp, num_splits=0, flags=0, max_splits=None, max_context_len=None, relayout=None):
+    def __init__(self, inp, num_splits=0, flags=0, max_splits=None, max_context_len=None, relayout=None,
+                 lens=False):
         import torch
         validate_inputs(inp)
         self.inp = inp
@@ -46,8 +47,13 @@ class Decode:
         mx = int(max(inp.context_lens)) if len(inp.context_lens) else 0
         if max_context_len is not None:
             mx = max_context_len
-        self.plan = sk.attn_decode_plan(self.desc, mx, max_splits or num_splits, flags)
+        if lens:     # the batch's lengths known on the host: the policy may fix one split length
+            self.plan = sk.attn_decode_plan_lens(self.desc, [int(x) for x in inp.context_lens],
+                                                 max_splits or num_splits, flags)
+        else:
+            self.plan = sk.attn_decode_plan(self.desc, mx, max_splits or num_splits, flags)
         self.S = num_splits or self.plan.num_splits
+        self.chunk = self.plan.split_chunk or None   # fixed split length, for the oracle's split rule
         self.dtype = torch.float32 if w.kv_dtype == "f32" else torch.bfloat16
         self.ws = torch.empty(self.plan.workspace_bytes // 4, dtype=torch.float32, device="cuda")
         # With the in-kernel merge the workspace starts with its counters,

@@ -335,3 +335,92 @@ def test_xcd_order_only_for_batched_single_position_decode():
     assert sk.attn_decode_plan(desc(B=1), 65536, 0).xcd_remap == 0
     assert sk.attn_decode_plan(desc(B=4, q_len=4, causal=1, maxp=2048), 2048, 0).xcd_remap == 0
     assert sk.attn_decode_plan(mla_desc(48), 68000, 0, sk.ATTN_PLAN_NO_XCD_REMAP).xcd_remap == 0
+
+
+def drafts_desc(B=6):
+    return desc(B=B, q_len=4, Hq=32, Hkv=4, Dk=256, Dv=256, P=16, maxp=128, causal=1, pages=768)
+
+
+def test_plan_lens_fixes_one_split_length_for_ragged_batches():
+    """Known lengths: the policy gives every request the same split length
+    (in proportion to its length, per-request split counts) when that
+    shortens the longest walk and the live workgroups fit one round."""
+    lens = [256, 512, 768, 1024, 1536, 2048]
+    p = sk.attn_decode_plan_lens(drafts_desc(), lens, 0, 0)
+    assert p.split_chunk == 128 and p.num_splits == 16 and p.max_splits == 16
+    # the work list: one (request, split) item per 128 keys, request-major
+    assert list(p.split_start[:7]) == [0, 2, 6, 12, 20, 32, 48] and p.live_splits == 48
+    assert all(x == 0 for x in p.split_start[7:])
+    assert p.live_splits * 4 * p.head_tiles == 192 <= 256
+    # the split-count rule for the same batch walks 256 keys per split
+    q = sk.attn_decode_plan(drafts_desc(), 2048, 0)
+    assert q.split_chunk == 0 and q.num_splits == 8
+    b, e = sk.attn_decode_split_range(q, 2048, 0, 0)
+    assert e - b == 256
+    assert p.key != q.key
+    # every request's splits follow the oracle's fixed-length rule
+    for L in list(range(0, 2049, 7)) + lens:
+        ref = oracle.split_bounds(L, p.num_splits, 64, chunk=p.split_chunk)
+        for s in range(p.num_splits):
+            assert sk.attn_decode_split_range(p, L, 0, s) == ref[s], (L, s)
+
+
+def test_plan_lens_on_equal_lengths_equals_plan():
+    for d, lens in ((mla_desc(48), [68000] * 48), (desc(), [65536]), (desc(B=3, maxp=2048), [2048] * 3),
+                    (desc(B=64, Hq=128, Hkv=1, Dk=576, Dv=512, P=1, maxp=16384, alias=1, pages=1 << 20),
+                     [16384] * 64)):
+        a = sk.attn_decode_plan_lens(d, lens, 0, 0).as_dict()
+        b = sk.attn_decode_plan(d, max(lens), 0, 0).as_dict()
+        assert a == b
+
+
+def test_plan_lens_forced_and_p2_splits_keep_the_split_count_rule():
+    lens = [256, 512, 768, 1024, 1536, 2048]
+    for n, f in ((5, 0), (0, sk.ATTN_PLAN_POLICY_P2)):
+        a = sk.attn_decode_plan_lens(drafts_desc(), lens, n, f)
+        assert a.split_chunk == 0
+        assert a.as_dict() == sk.attn_decode_plan(drafts_desc(), 2048, n, f).as_dict()
+
+
+def test_fixed_split_length_plans_run_with_their_own_split_count():
+    p = sk.attn_decode_plan_lens(drafts_desc(), [256, 512, 768, 1024, 1536, 2048], 0, 0)
+    fake = 1 << 20
+    for S in (1, 8, 15):
+        with pytest.raises(sk.AttnDecodeError) as ei:
+            sk.attn_decode_run(p, fake, fake, fake, fake, fake, 0.1, S, fake, None, fake, 1 << 30, stream=0)
+        assert ei.value.status == sk.ATTN_EINVAL
+        with pytest.raises(sk.AttnDecodeError) as ei:
+            sk.attn_decode_split_range(p, 100, S, 0)
+        assert ei.value.status == sk.ATTN_EINVAL
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_run(p, fake, fake, fake, fake, fake, 0.1, 17, fake, None, fake, 1 << 30, stream=0)
+    assert ei.value.status == sk.ATTN_EWORKSPACE
+
+
+def test_plan_lens_argument_errors():
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_plan_lens(drafts_desc(), [256, -1, 3, 4, 5, 6], 0, 0)
+    assert ei.value.status == sk.ATTN_EINVAL
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_plan_lens(drafts_desc(), [256, 100000, 3, 4, 5, 6], 0, 0)   # beyond the page table
+    assert ei.value.status == sk.ATTN_EINVAL
+    L = sk.lib()
+    st = L.attn_decode_plan_lens(ctypes.byref(drafts_desc()), None, 0, 0, ctypes.byref(sk.AttnDecodePlan()))
+    assert st == sk.ATTN_EINVAL
+
+
+def test_split_table_only_for_small_unfused_batches():
+    """The work list lives in the plan (ATTN_MAX_SPLIT_TABLE requests) and
+    the in-kernel merge counts a fixed number of splits per row group, so
+    larger batches and fused plans keep the split-count rule."""
+    lens = [256, 512, 768, 1024, 1536, 2048] * 11                 # 66 requests
+    d = desc(B=66, q_len=4, Hq=32, Hkv=4, Dk=256, Dv=256, P=16, maxp=128, causal=1, pages=10000)
+    p = sk.attn_decode_plan_lens(d, lens, 0, 0)
+    assert p.split_chunk == 0 and p.live_splits == 0
+    f = sk.attn_decode_plan_lens(drafts_desc(), [256, 512, 768, 1024, 1536, 2048], 0, sk.ATTN_PLAN_FUSED_MERGE)
+    assert f.split_chunk == 0 and f.live_splits == 0
+    # zero-length requests own no work item
+    z = sk.attn_decode_plan_lens(drafts_desc(), [0, 512, 0, 1024, 1536, 2048], 0, 0)
+    assert z.split_chunk > 0
+    st = list(z.split_start[:7])
+    assert st[1] - st[0] == 0 and st[3] - st[2] == 0 and z.live_splits == st[6]

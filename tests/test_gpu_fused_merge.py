@@ -119,14 +119,19 @@ def test_fused_graph_replays_match_eager(name):
         assert (d.counters() == 0).all(), r
 
 
-@pytest.mark.parametrize("name,S,requests", [("varlen_drafts", None, None), ("mla_b48", None, (0, 13, 47)),
-                                             ("mla_wide", None, (0, 63)), ("gqa_64k", 64, None),
-                                             ("prefill_varlen_d64", 8, None)])
-def test_fused_full_size_sampled(name, S, requests):
+@pytest.mark.parametrize("name,S,requests,lens", [("varlen_drafts", None, None, False),
+                                                  ("varlen_drafts", None, None, True),
+                                                  ("mla_b48", None, (0, 13, 47), False),
+                                                  ("mla_wide", None, (0, 63), False), ("gqa_64k", 64, None, False),
+                                                  ("prefill_varlen_d64", 8, None, False)])
+def test_fused_full_size_sampled(name, S, requests, lens):
+    # lens: planned with the batch's lengths; a fused plan keeps the
+    # split-count rule (its counters expect the same split count per row group)
     w = get(name)
-    say(f"fused full-size {name}: generating inputs")
+    say(f"fused full-size {name} lens={lens}: generating inputs")
     inp = generate(w)
-    d = Decode(inp, num_splits=S or 0, flags=FUSED)
+    d = Decode(inp, num_splits=S or 0, flags=FUSED, lens=lens)
+    assert d.chunk is None and d.plan.live_splits == 0
     assert 2 <= d.S <= 64, d.S
     say(f"fused full-size {name}: run S={d.S}")
     d.run()

@@ -51,6 +51,11 @@ def small_cases():
         # fp32 runs on the vector ALUs: 8 and 16 rows at head dim 128
         "gqa_f32_g8": scaled("gqa_64k", context_lens=(3000, 1, 777), kv_dtype="f32", seed=28),
         "gqa_f32_g16": scaled("gqa_64k", context_lens=(2100, 300), num_q_heads=32, kv_dtype="f32", seed=31),
+        # ragged batches whose plans with known lengths take a fixed split
+        # length (192 keys for both)
+        "gqa_bf16_ragged8": scaled("gqa_64k", context_lens=(9000, 100, 3000, 6000, 1, 12000, 500, 7000), seed=38),
+        "gqa_f32_ragged6": scaled("gqa_64k", context_lens=(20000, 1000, 5000, 300, 12000, 7000), kv_dtype="f32",
+                                  seed=39),
     }
 
 
@@ -73,17 +78,33 @@ def check_against_oracle(d: Decode, tol, S=None, requests=None, check_splits=Tru
     assert e_out <= tol, f"output rel err {e_out:.3e} > {tol}"
     assert e_lse <= 1e-3, f"lse err {e_lse:.3e}"
     if check_splits and d.partials_written:
-        po, pl = oracle.split_reference(inp, S, requests=requests)
+        po, pl = oracle.split_reference(inp, S, requests=requests, chunk=d.chunk)
         go, gl = d.split_parts(S)
+        if d.plan.live_splits > 0:
+            # split table: request b writes its first n_b slots only; the
+            # oracle's later splits must hold no key (the table covers all)
+            for b in (range(inp.w.batch) if requests is None else requests):
+                n_b = d.plan.split_start[b + 1] - d.plan.split_start[b]
+                assert np.all(np.isneginf(pl[b, ..., n_b:])), b
+                go[b, ..., n_b:, :] = po[b, ..., n_b:, :]
+                gl[b, ..., n_b:] = pl[b, ..., n_b:]
         gl_ = gl[sel]
         go_ = go[sel]
         e_po = row_rel_err(go_, po[sel])
         e_pl = lse_err(gl_, pl[sel])
         assert e_po <= tol, f"per-split output rel err {e_po:.3e}"
         assert e_pl <= 1e-3, f"per-split lse err {e_pl:.3e}"
-        # planted mistake in the oracle: a split rule on 32-key blocks must not
+        # planted mistake in the oracle: a split rule on 32-key blocks (a split
+        # length 64 keys longer, for a plan with a fixed split length) must not
         # agree with the kernel wherever the two rules differ
-        if S > 1:
+        lens_sel = inp.context_lens if requests is None else inp.context_lens[list(requests)]
+        if S > 1 and d.chunk:
+            bo, bl = oracle.split_reference(inp, S, requests=requests, chunk=d.chunk + 64)
+            if any(int(L) > d.chunk for L in lens_sel):
+                fin = np.isfinite(bl[sel]) & np.isfinite(gl_)
+                assert np.max(np.abs(bl[sel][fin] - gl_[fin]), initial=0) > 1e-3 or \
+                    np.isneginf(bl[sel]).sum() != np.isneginf(gl_).sum()
+        elif S > 1:
             bo, bl = oracle.split_reference(inp, S, A=32, requests=requests)
             differs = any(oracle.split_bounds(int(L), S, 32) != oracle.split_bounds(int(L), S, 64)
                           for L in (inp.context_lens if requests is None else inp.context_lens[list(requests)]))
@@ -92,6 +113,22 @@ def check_against_oracle(d: Decode, tol, S=None, requests=None, check_splits=Tru
                 assert np.max(np.abs(bl[sel][fin] - gl_[fin]), initial=0) > 1e-3 or \
                     np.isneginf(bl[sel]).sum() != np.isneginf(gl_).sum()
     return e_out, e_lse
+
+
+# ragged batches planned with their lengths known on the host: the policy
+# gives every request the same split length (per-request split counts)
+LENS_CASES = ["gqa_64k_b3_ragged", "mla_wide_b4", "varlen_drafts", "d256_g8", "prefill_small_d64",
+              "gqa_bf16_ragged8", "gqa_f32_ragged6"]
+
+
+@pytest.mark.parametrize("name", LENS_CASES)
+def test_parity_small_lens_plans(name):
+    w = small_cases()[name]
+    inp = inputs(name, w)
+    say(f"parity_small lens plan {name} B={w.batch} ctx={w.context_lens[:6]} run")
+    d = Decode(inp, lens=True).run()
+    e_out, e_lse = check_against_oracle(d, tol_for(w))
+    print(f"{name}: S={d.S} chunk={d.plan.split_chunk} out {e_out:.2e} lse {e_lse:.2e}")
 
 
 @pytest.mark.parametrize("name", list(small_cases()))
@@ -293,7 +330,7 @@ def test_empty_contexts_and_splits():
     assert np.all(out[4] == 0) and np.all(np.isneginf(lse[4]))
 
 
-def designated_tokens(inp, S, where):
+def designated_tokens(inp, S, where, chunk=None):
     """Per request and KV head, one designated key per split: the first or
     the last key every query row of the request can see in that split."""
     w = inp.w
@@ -304,7 +341,7 @@ def designated_tokens(inp, S, where):
         per_head = []
         for h in range(w.num_kv_heads):
             ts = []
-            for (sb, se) in oracle.split_bounds(L, S):
+            for (sb, se) in oracle.split_bounds(L, S, chunk=chunk):
                 e = min(se, n0)
                 if e <= sb:
                     continue
@@ -317,22 +354,28 @@ def designated_tokens(inp, S, where):
     return toks
 
 
-@pytest.mark.parametrize("name", ["gqa_tiny_f32", "gqa_64k_b3_ragged", "mla_b48_b16", "mla_wide_b4",
-                                  "varlen_drafts", "mla_h4", "d256_g8", "gqa_f32_g16", "gqa_d64_bf16"])
+@pytest.mark.parametrize("name,lens", [(n, False) for n in (
+    "gqa_tiny_f32", "gqa_64k_b3_ragged", "mla_b48_b16", "mla_wide_b4", "varlen_drafts", "mla_h4", "d256_g8",
+    "gqa_f32_g16", "gqa_d64_bf16")] + [(n, True) for n in (
+    "mla_wide_b4", "varlen_drafts", "d256_g8", "gqa_bf16_ragged8", "gqa_f32_ragged6")])
 @pytest.mark.parametrize("where", ["first", "last"])
-def test_bitexact_gather_and_boundaries(name, where):
+def test_bitexact_gather_and_boundaries(name, lens, where):
     """One-hot: the designated key of each split scores 2*dims above all
     others, so its weight is exactly 1 and every other weight is 0; each
-    split's o_part must then be that key's V row bit for bit."""
+    split's o_part must then be that key's V row bit for bit.  lens: plans
+    made with the batch's lengths (one fixed split length per request)."""
     w = small_cases()[name]
     base = inputs(name, w)
-    probe = Decode(base, num_splits=w.num_splits)
-    S = probe.S
+    probe = Decode(base, num_splits=w.num_splits, lens=lens)
+    S, chunk = probe.S, probe.chunk
     del probe
-    toks = designated_tokens(base, S, where)
+    if lens:
+        assert chunk, f"{name}: the lens plan kept the split-count rule"
+    toks = designated_tokens(base, S, where, chunk)
     inp = designate(base, toks)
-    say(f"bitexact {name} {where} S={S}")
-    d = Decode(inp, num_splits=S).run()
+    say(f"bitexact {name} lens={lens} {where} S={S} chunk={chunk}")
+    d = Decode(inp, num_splits=S if not lens else 0, lens=lens).run()
+    assert d.S == S and d.chunk == chunk
     if S == 1:
         d.partials()
     go, gl = d.split_parts()
@@ -342,7 +385,7 @@ def test_bitexact_gather_and_boundaries(name, where):
     checked = 0
     for b in range(w.batch):
         L = int(inp.context_lens[b])
-        bounds = oracle.split_bounds(L, S)
+        bounds = oracle.split_bounds(L, S, chunk=chunk)
         for kvh in range(w.num_kv_heads):
             for t in toks[b][kvh]:
                 s = next(i for i, (sb, se) in enumerate(bounds) if sb <= t < se)
@@ -491,7 +534,8 @@ def test_stage2_alone_on_random_partials(S, Hq, dtype):
     assert lse_err(lse.double().cpu().numpy(), ml) <= 1e-5
 
 
-# ---- full sizes, policy split count (the launch configuration the benchmark times) ----
+# ---- full sizes, policy split count with the batch's lengths known on the host
+# (the launch configuration the benchmark times) ----
 
 FULL = [("gqa_64k", None), ("gqa_64k_d64", None), ("varlen_drafts", None), ("prefill_2048x4_d64", None),
         ("prefill_2048x4_d128", (0, 3)), ("prefill_varlen_d64", None), ("prefill_varlen_d128", None),
@@ -505,7 +549,7 @@ def test_parity_full_size_sampled(name, requests):
     say(f"full-size {name}: generating inputs")
     inp = generate(w)
     say(f"full-size {name}: run")
-    d = Decode(inp).run()
+    d = Decode(inp, lens=True).run()
     e_out, e_lse = check_against_oracle(d, tol_for(w), requests=requests)
     print(f"{name}: S={d.S} out {e_out:.2e} lse {e_lse:.2e}")
     if requests is not None:
