@@ -69,11 +69,12 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(w, S):
+def algorithmic_bytes(w, S, split_counts=None):
     """Bytes one stage-1 launch must move at minimum: every visible key of
     every KV head once (V counted once when it aliases K), the page-table
     entries, q, and the partial outputs + log-sum-exps it writes (with one
-    split: the output and log-sum-exp themselves)."""
+    split: the output and log-sum-exp themselves; with a work list,
+    split_counts[b] partials per row of request b)."""
     es = w.elem_bytes
     kv = w.logical_kv_bytes()
     pt = sum(-(-c // w.page_size) for c in w.context_lens) * 4
@@ -82,7 +83,12 @@ def algorithmic_bytes(w, S):
     seen = sum(min(w.q_len, L) if w.causal else (w.q_len if L > 0 else 0) for L in w.context_lens)
     q = seen * w.num_q_heads * w.head_dim_qk * es
     rows = w.batch * w.q_len * w.num_q_heads
-    part = rows * S * (w.head_dim_v + 1) * 4 if S > 1 else rows * (w.head_dim_v * es + 4)
+    if S == 1:
+        part = rows * (w.head_dim_v * es + 4)
+    elif split_counts is not None:
+        part = sum(split_counts) * w.q_len * w.num_q_heads * (w.head_dim_v + 1) * 4
+    else:
+        part = rows * S * (w.head_dim_v + 1) * 4
     return kv, kv + pt + q + part
 
 
@@ -255,7 +261,10 @@ def measure(w, args, stream, splits=0, flags=0, want_inputs=False):
     # one fixed split length for every request)
     plan = sk.attn_decode_plan_lens(desc, [int(x) for x in w.context_lens], splits or w.num_splits, flags)
     S = plan.num_splits
-    kv_bytes, alg_bytes = algorithmic_bytes(w, S)
+    counts = None
+    if plan.live_splits > 0:   # work list: request b writes its own split count's partials
+        counts = [plan.split_start[b + 1] - plan.split_start[b] for b in range(w.batch)]
+    kv_bytes, alg_bytes = algorithmic_bytes(w, S, counts)
     touched = w.unique_kv_bytes()
     R = args.replicas or max(1, -(-(1 << 30) // touched))
     ks = [t["k_cache"]] + [t["k_cache"].clone() for _ in range(R - 1)]
@@ -327,7 +336,7 @@ def measure(w, args, stream, splits=0, flags=0, want_inputs=False):
         "num_splits": S, "split_chunk": plan.split_chunk, "rows_per_wg": plan.rows_per_wg,
         "head_tiles": plan.head_tiles,
         "stage1_waves": plan.stage1_waves, "xcd_remap": plan.xcd_remap, "plan_flags": plan.flags,
-        "replicas": R, "kv_bytes_per_op": kv_bytes,
+        "replicas": R, "kv_bytes_per_op": kv_bytes, "plan_key": str(plan.key),
         "roofline": {"bound": "hbm", "kernel": "stage1", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": flops,
@@ -391,6 +400,7 @@ def main():
                    "rows_per_wg": head["rows_per_wg"],
                    "head_tiles": head["head_tiles"], "stage1_waves": head["stage1_waves"],
                    "xcd_remap": head["xcd_remap"], "plan_flags": head["plan_flags"], "replicas": head["replicas"],
+                   "plan_key": head["plan_key"],
                    "kv_bytes_per_op": kv_bytes, "parallelism": "single GPU"},
         "tflops_per_s": head["tflops_per_s"],
         "roofline": head["roofline"],

@@ -27,3 +27,12 @@ def test_bytes_count_each_kv_row_once(name):
     assert total > kv + rows * 4 * (w.head_dim_v + 1) * 4 - 1      # partials of 4 splits included
     _, one = bench.algorithmic_bytes(w, 1)
     assert one < total                                               # one split: the output instead
+
+
+def test_bytes_count_only_the_work_lists_partials():
+    w = CONFIGS["varlen_drafts"]
+    counts = [2, 4, 6, 8, 12, 16]           # 128-key splits of the drafts' lengths
+    kv, dense = bench.algorithmic_bytes(w, 16)
+    _, listed = bench.algorithmic_bytes(w, 16, counts)
+    per_split_row = w.q_len * w.num_q_heads * (w.head_dim_v + 1) * 4
+    assert dense - listed == (16 * w.batch - sum(counts)) * per_split_row
