@@ -33,7 +33,7 @@ class Decode:
     """One uploaded problem + plan; run() calls attn_decode_run."""
 
     def __init__(self, inp, num_splits=0, flags=0, max_splits=None, max_context_len=None, relayout=None,
-                 lens=False):
+                 lens=False, host_lens=None):
         import torch
         validate_inputs(inp)
         self.inp = inp
@@ -48,8 +48,8 @@ class Decode:
         if max_context_len is not None:
             mx = max_context_len
         if lens:     # the batch's lengths known on the host: the policy may fix one split length
-            self.plan = sk.attn_decode_plan_lens(self.desc, [int(x) for x in inp.context_lens],
-                                                 max_splits or num_splits, flags)
+            hl = [int(x) for x in (inp.context_lens if host_lens is None else host_lens)]
+            self.plan = sk.attn_decode_plan_lens(self.desc, hl, max_splits or num_splits, flags)
         else:
             self.plan = sk.attn_decode_plan(self.desc, mx, max_splits or num_splits, flags)
         self.S = num_splits or self.plan.num_splits

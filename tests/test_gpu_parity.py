@@ -131,6 +131,27 @@ def test_parity_small_lens_plans(name):
     print(f"{name}: S={d.S} chunk={d.plan.split_chunk} out {e_out:.2e} lse {e_lse:.2e}")
 
 
+@pytest.mark.parametrize("name,device_lens", [
+    ("varlen_drafts", (200, 512, 3, 1000, 0, 2048)),
+    ("gqa_bf16_ragged8", (9000, 0, 2999, 6000, 1, 11800, 64, 129)),
+    ("gqa_f32_ragged6", (19999, 1000, 1, 300, 12000, 6500)),
+    ("d256_g8", (1, 2049, 0))])
+def test_lens_plan_with_shorter_device_lengths(name, device_lens):
+    """A work-list plan made for the host lengths, run on device lengths
+    that are each no longer (the documented precondition): the splits past
+    a shorter request's keys are empty and the result is the attention over
+    the device lengths."""
+    w = small_cases()[name]
+    base = inputs(name, w)
+    assert all(d <= h for d, h in zip(device_lens, w.context_lens))
+    inp = base.with_(context_lens=np.asarray(device_lens, np.int32))
+    say(f"lens plan {name}: host {w.context_lens} device {device_lens}")
+    d = Decode(inp, lens=True, host_lens=w.context_lens).run()
+    assert d.chunk and d.plan.live_splits > 0
+    e_out, e_lse = check_against_oracle(d, tol_for(w))
+    print(f"{name}: S={d.S} chunk={d.chunk} out {e_out:.2e} lse {e_lse:.2e}")
+
+
 @pytest.mark.parametrize("name", list(small_cases()))
 def test_parity_small(name):
     w = small_cases()[name]
