@@ -135,10 +135,16 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 20}), flush=True)
 
 
+WARM_SECONDS = 0.3   # untimed replays before the timed ones: the part's clocks ramp up over this
+
+
 def time_graph(fn_steps, steps, stream, rounds=5):
-    """Capture fn_steps(i) for i < steps into one graph; replay it `rounds`
-    times, each between HIP events; return (median ms per replay, graph,
-    every replay's ms)."""
+    """Capture fn_steps(i) for i < steps into one graph; replay it untimed
+    for WARM_SECONDS (graph upload, first touches, and the clock ramp: on
+    the compute-heavier configs successive replays ran up to 10% faster
+    over the first few hundred milliseconds), then `rounds` times, each
+    between HIP events; return (median ms per replay, graph, every replay's
+    ms)."""
     import statistics
 
     import torch
@@ -149,8 +155,12 @@ def time_graph(fn_steps, steps, stream, rounds=5):
     torch.cuda.synchronize()
     times = []
     with torch.cuda.stream(stream):     # replay() launches on the current stream
-        g.replay()                      # untimed replay (graph upload, first touches)
-        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while True:                     # untimed replays
+            g.replay()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= WARM_SECONDS:
+                break
         for _ in range(rounds):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
