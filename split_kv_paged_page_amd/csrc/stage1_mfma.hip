@@ -20,6 +20,11 @@ constexpr MfmaEntry kTable[] = {
     mfma_entry<256, 256, false, 2, 1>(32),
     mfma_entry<256, 256, false, 1, 4>(16),
     mfma_entry<256, 256, false, 1, 1>(1),
+    // 128+ rows (prefill): each block in LDS serves twice the rows of the
+    // four-tile shape, which halves the key reads per row out of the L2;
+    // prefill 4 x 2048 stage 1 90.0 -> 87.5 us, varlen 67.4 -> 63.0.  With
+    // a ring of 2 tiles it was no faster (88.0, 68.7).
+    mfma_entry<128, 128, false, 8, 1>(128),
     mfma_entry<128, 128, false, 4, 1>(64),
     mfma_entry<128, 128, false, 1, 4>(16),
     mfma_entry<128, 128, false, 1, 1>(1),

@@ -11,9 +11,9 @@
 // take the split's 32-key blocks in turn with their own tile and running max
 // / sum / accumulators, merged at the end.  Shapes, by rows per KV head:
 //   * 64+ (wide MLA; prefill, where every query position of a GQA group is
-//     a row), 32 (draft groups): 4 or 2 tiles on a ring of 3 (two blocks in
-//     flight; a ring of 2 for the four tiles at head dim 128), each block
-//     read once per 64 or 32 rows;
+//     a row; 128+ at head dim 128 takes 8 tiles), 32 (draft groups): 8, 4 or
+//     2 tiles on a ring of 3 (two blocks in flight; a ring of 2 for the four
+//     tiles at head dim 128), each block read once per 128, 64 or 32 rows;
 //   * 16 (MLA bh16): one tile, four key streams, load -> wait -> compute;
 //   * 1-15 (GQA, MLA with few heads): one wave alone on a ring of 3 (two
 //     blocks in flight); 25 KB of LDS at head dim 64 and 49 KB at 128 (two

@@ -141,9 +141,10 @@ def test_kernel_choice_by_rows_per_kv_head():
         assert (p.variant, p.rows_per_wg, p.stage1_waves) == want, (hq, want)
     assert sk.attn_decode_plan(desc(Hq=16, Dk=64, Dv=64), 4096, 0).variant == M     # bf16 head dim 64
     # causal prefill rows (query positions x group) at head dims 64 and 128: four 16-row waves sharing
-    # each block from 64 rows on, four key streams from 16
+    # each block from 64 rows on (eight from 128 at head dim 128), four key streams from 16
     for d in (64, 128):
-        for q_len, want in ((4, (M, 16, 4)), (15, (M, 16, 4)), (16, (M, 64, 4)), (2048, (M, 64, 4))):
+        wide = (M, 128, 8) if d == 128 else (M, 64, 4)
+        for q_len, want in ((4, (M, 16, 4)), (15, (M, 16, 4)), (16, (M, 64, 4)), (2048, wide)):
             p = sk.attn_decode_plan(desc(Hq=16, Hkv=4, q_len=q_len, Dk=d, Dv=d, causal=1), 4096, 0)
             assert (p.variant, p.rows_per_wg, p.stage1_waves) == want, (d, q_len, want)
     with pytest.raises(sk.AttnDecodeError):      # no kernel at head dim 96
