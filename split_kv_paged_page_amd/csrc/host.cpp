@@ -26,7 +26,7 @@ attn_status hip_fail(hipError_t e, const char* what) {
   return fail(ATTN_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
-constexpr int kSplitAlign = 64;   // keys per stage-1 block and split granule
+constexpr int kSplitAlign = 64;   // split granule in keys (the VALU kernel's block; two matrix-core blocks)
 constexpr int kNumCu = 256;       // MI355X compute units
 constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kMaxSplits = 4096;  // far above any useful split count; bounds the workspace
