@@ -444,12 +444,17 @@ def main():
 
 
 def source_hash() -> str:
+    """Hash of the library's sources without their // comments and blank
+    lines (the sources hold no block comments and no "//" inside strings),
+    so that counters taken on a build stay matched to it across comment
+    edits."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "split_kv_paged_page_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            code = [ln.split("//", 1)[0].rstrip() for ln in fh]
+        h.update(f.encode() + "\n".join(ln for ln in code if ln).encode())
     return h.hexdigest()[:16]
 
 
