@@ -96,9 +96,9 @@ enum {
                                        #4758, Motivation, batch-1 paragraph).  Matrix-core
                                        plans only; the workspace counters need
                                        attn_decode_workspace_init.  Off by default: on
-                                       MI355X the per-XCD L2 write-back each workgroup's
-                                       release costs, and the merge on one CU per group,
-                                       outweigh the launch it saves */
+                                       MI355X merging a whole group's partials on one CU
+                                       (with the per-XCD L2 write-back of each release)
+                                       takes longer than the launch it saves */
 };
 
 /* Kernel families the planner picks from. */
