@@ -57,6 +57,9 @@ def parse():
                     help="comma-separated workloads timed after the headline one, each reported under "
                          "'configs' ('' for none)")
     ap.add_argument("--splits", type=int, default=0, help="force the split count (0: planner policy)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="the workload with B requests of its first request's length (the aiter PR's "
+                         "concurrency sweep; 0: as named)")
     ap.add_argument("--flags", type=int, default=0, help="attn_decode_plan flags")
     ap.add_argument("--replicas", type=int, default=0, help="KV pool copies to rotate (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -378,10 +381,13 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
-    from workloads import get
+    from workloads import get, scaled
 
     stream = torch.cuda.Stream()
     w = get(args.config)
+    if args.batch:   # same requests, B of them; the page pool in proportion (at least what they take)
+        w = scaled(args.config, batch=args.batch, pool_pages=-(-w.pool_pages * args.batch // w.batch))
+        w = scaled(args.config, batch=args.batch, pool_pages=max(w.pool_pages, w.pages_needed()))
     head, inp = measure(w, args, stream, args.splits, args.flags, want_inputs=not args.no_cpu_baseline)
     kv_bytes = head["kv_bytes_per_op"]
     us_op, us_s1 = head["us_per_op"], head["stage1_us"]

@@ -94,6 +94,17 @@ class Workload:
         per request (shared prefixes are counted once per request)."""
         return sum(self.context_lens) * self.num_kv_heads * self.kv_bytes_per_token_head()
 
+    def pages_needed(self) -> int:
+        """Pool pages the page tables take: each group's prefix once, then
+        every request's pages past it (see gen.page_table_for)."""
+        P = self.page_size
+        need = [-(-L // P) for L in self.context_lens]
+        if not self.prefix_group:
+            return sum(need)
+        npp = self.prefix_len // P
+        groups = -(-self.batch // self.prefix_group)
+        return groups * npp + sum(max(0, n - npp) for n in need)
+
     def unique_kv_bytes(self) -> int:
         if not self.prefix_group:
             return self.logical_kv_bytes()

@@ -96,6 +96,8 @@ def page_table_for(w: Workload, perm: np.ndarray) -> np.ndarray:
     group's prefix pages are taken first, then every request's private pages.
     """
     P = w.page_size
+    if w.pages_needed() > w.pool_pages:
+        raise ValueError(f"{w.name}: pool of {w.pool_pages} pages is smaller than the {w.pages_needed()} needed")
     pt = np.zeros((w.batch, w.max_pages_per_req), dtype=np.int32)
     cur = 0
     prefix_pages = {}
@@ -117,8 +119,7 @@ def page_table_for(w: Workload, perm: np.ndarray) -> np.ndarray:
         else:
             pt[b, :need] = perm[cur:cur + need]
             cur += need
-    if cur > w.pool_pages:
-        raise ValueError(f"{w.name}: pool of {w.pool_pages} pages is smaller than the {cur} needed")
+    assert cur == w.pages_needed()
     return pt
 
 
