@@ -90,7 +90,12 @@ struct MCfg {
   static constexpr int TILE = ((KTILE + VTILE) + 255) / 256 * 256;
   static constexpr int TILES = KW * NBUF * TILE;
   static constexpr int PIDS = NBUF > 1 ? NW * NBUF * 256 : 0;  // per-wave page-id ring (ring path only)
-  static constexpr int PART = 16 * DV * 4 + 2 * 16 * 4;  // merge state: acc [16][DV], m[16], l[16]
+  // Merge state of a key stream: acc [16][RS], m[16], l[16].  The row
+  // stride is padded by 16 bytes so that a write of the 16 rows' 16-byte
+  // pieces (lane n: row n) touches all 64 banks once; unpadded, the rows sat
+  // a multiple of 256 bytes apart and every write was 16 lanes deep per bank.
+  static constexpr int RS = DV + 4;
+  static constexpr int PART = 16 * RS * 4 + 2 * 16 * 4;
   static constexpr int PARTS = KW > 1 ? NW * PART : 0;   // only key streams need merging
   static constexpr int SMEM = TILES + PIDS > PARTS ? TILES + PIDS : PARTS;
   static_assert(KCH % 4 == 0 && VCH % 4 == 0, "row sizes");
@@ -659,14 +664,15 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
                   make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv), lse);
     }
   } else {
-    // ---- wave state into LDS: acc^T [16 rows][DV], m[16], l[16] ----
+    // ---- wave state into LDS: acc^T [16 rows][RS], m[16], l[16] ----
     __syncthreads();  // the tiles are no longer read
+    constexpr int RS = C::RS;
     float* pacc = (float*)(smem + wave * C::PART);
-    float* pml = pacc + 16 * DV;
+    float* pml = pacc + 16 * RS;
     // Lane l holds O^T[dims dt*16 + 4g + i][row n].
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
-      *(float4*)(pacc + n * DV + dt * 16 + 4 * g) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+      *(float4*)(pacc + n * RS + dt * 16 + 4 * g) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
     if (g == 0) {
       pml[n] = m;
       pml[16 + n] = l;
@@ -682,7 +688,7 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
       float M = kNegInf;
 #pragma unroll
       for (int w = 0; w < KW; ++w)
-        M = fmaxf(M, ((const float*)(smem + (w * RW + rt) * C::PART))[16 * DV + r]);
+        M = fmaxf(M, ((const float*)(smem + (w * RW + rt) * C::PART))[16 * RS + r]);
       float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
       float lse = kNegInf;
       if (M != kNegInf) {
@@ -691,9 +697,9 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
 #pragma unroll
         for (int w = 0; w < KW; ++w) {
           const float* base = (const float*)(smem + (w * RW + rt) * C::PART);
-          const float f = fast_exp2(base[16 * DV + r] - M);
-          den += f * base[16 * DV + 16 + r];
-          const float4 a = *(const float4*)(base + r * DV + d);
+          const float f = fast_exp2(base[16 * RS + r] - M);
+          den += f * base[16 * RS + 16 + r];
+          const float4 a = *(const float4*)(base + r * RS + d);
           num.x += f * a.x;
           num.y += f * a.y;
           num.z += f * a.z;
