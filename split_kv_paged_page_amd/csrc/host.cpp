@@ -343,9 +343,13 @@ attn_status plan_impl(const attn_decode_desc* desc, int32_t max_context_len, con
   p.xcd_remap = (flags & ATTN_PLAN_NO_XCD_REMAP) || d.q_len > 1 || d.batch == 1 ? 0 : 1;
   // bf16 runs on the matrix cores at every group size (a 16-row tile part
   // empty still costs a fraction of the vector-ALU work per key); fp32 runs
-  // on the vector ALUs.
+  // on the vector ALUs.  One request takes a ring shape where several would
+  // take key streams (16-63 rows): the streams' four waves compute four
+  // blocks at once but load each block only when its wave is free, which
+  // pays when many requests re-read shared prefix pages from the L2, and
+  // nothing shares pages within one request.
   const splitkv::MfmaShape ms =
-      splitkv::stage1_mfma_shape(d.dtype, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0, rows);
+      splitkv::stage1_mfma_shape(d.dtype, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0, rows, d.batch > 1);
   int wgs_per_cu = 2;
   if (ms.rw > 0) {
     p.variant = ATTN_VARIANT_MFMA;

@@ -86,7 +86,8 @@ hipError_t launch_stage1_valu(const Stage1Params& p, int dtype, int dk, int dv, 
 struct MfmaShape {
   int rw, kw, smem;
 };
-MfmaShape stage1_mfma_shape(int dtype, int dk, int dv, bool v_aliases_k, int rows);
+// streams = false: no key-stream shape (kw > 1); the ring shapes serve the rows.
+MfmaShape stage1_mfma_shape(int dtype, int dk, int dv, bool v_aliases_k, int rows, bool streams = true);
 hipError_t launch_stage1_mfma(const Stage1Params& p, int dk, int dv, bool v_aliases_k, MfmaShape shape,
                               hipStream_t s);
 

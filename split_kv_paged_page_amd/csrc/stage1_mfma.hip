@@ -47,10 +47,10 @@ const MfmaEntry* find_entry(F&& f) {
 
 }  // namespace
 
-MfmaShape stage1_mfma_shape(int dtype, int dk, int dv, bool v_aliases_k, int rows) {
+MfmaShape stage1_mfma_shape(int dtype, int dk, int dv, bool v_aliases_k, int rows, bool streams) {
   if (dtype != 1) return MfmaShape{0, 0, 0};
   const MfmaEntry* e = find_entry([&](const MfmaEntry& x) {
-    return x.dk == dk && x.dv == dv && x.valias == v_aliases_k && rows >= x.min_rows;
+    return x.dk == dk && x.dv == dv && x.valias == v_aliases_k && rows >= x.min_rows && (streams || x.kw == 1);
   });
   return e ? MfmaShape{e->rw, e->kw, e->smem} : MfmaShape{0, 0, 0};
 }

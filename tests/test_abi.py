@@ -133,19 +133,24 @@ def test_kernel_choice_by_rows_per_kv_head():
         (dict(Hq=4, Hkv=1, Dk=64, Dv=64, dtype=F32), (V, 4, 4)),
     ]
     for kw, want in cases:
-        p = sk.attn_decode_plan(desc(**kw), 4096, 0)
+        p = sk.attn_decode_plan(desc(B=4, **kw), 4096, 0)
         assert (p.variant, p.rows_per_wg, p.stage1_waves) == want, (kw, want)
+        # one request: the ring shapes instead of key streams (one wave per 16-row tile)
+        p1 = sk.attn_decode_plan(desc(B=1, **kw), 4096, 0)
+        want1 = (M, 16, 1) if want[0] == M and want[2] == 4 and want[1] == 16 else want
+        assert (p1.variant, p1.rows_per_wg, p1.stage1_waves) == want1, (kw, want1)
     mla = dict(Hkv=1, Dk=576, Dv=512, P=1, maxp=68000, alias=1, pages=655360)
     for hq, want in ((4, (M, 16, 1)), (16, (M, 16, 4)), (128, (M, 64, 4))):
-        p = sk.attn_decode_plan(desc(Hq=hq, **mla), 68000, 0)
+        p = sk.attn_decode_plan(desc(B=48, Hq=hq, **mla), 68000, 0)
         assert (p.variant, p.rows_per_wg, p.stage1_waves) == want, (hq, want)
+    assert sk.attn_decode_plan(desc(B=1, Hq=16, **mla), 68000, 0).stage1_waves == 1
     assert sk.attn_decode_plan(desc(Hq=16, Dk=64, Dv=64), 4096, 0).variant == M     # bf16 head dim 64
     # causal prefill rows (query positions x group) at head dims 64 and 128: four 16-row waves sharing
     # each block from 64 rows on (eight from 128 at head dim 128), four key streams from 16
     for d in (64, 128):
         wide = (M, 128, 8) if d == 128 else (M, 64, 4)
         for q_len, want in ((4, (M, 16, 4)), (15, (M, 16, 4)), (16, (M, 64, 4)), (2048, wide)):
-            p = sk.attn_decode_plan(desc(Hq=16, Hkv=4, q_len=q_len, Dk=d, Dv=d, causal=1), 4096, 0)
+            p = sk.attn_decode_plan(desc(B=4, Hq=16, Hkv=4, q_len=q_len, Dk=d, Dv=d, causal=1), 4096, 0)
             assert (p.variant, p.rows_per_wg, p.stage1_waves) == want, (d, q_len, want)
     with pytest.raises(sk.AttnDecodeError):      # no kernel at head dim 96
         sk.attn_decode_plan(desc(Hq=16, Dk=96, Dv=96), 4096, 0)

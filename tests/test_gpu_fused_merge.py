@@ -28,7 +28,7 @@ FUSED = sk.ATTN_PLAN_FUSED_MERGE
 # contexts, causal drafts and prefill rows (the fp32 plans have no fused form)
 CASES = ["gqa_64k_s5000", "gqa_64k_b3_ragged", "mla_b48_b16", "mla_wide_b4", "varlen_drafts", "gqa_g4_bf16",
          "gqa_g20_bf16", "d256_g8", "mla_h4", "gqa_d64_bf16", "prefill_small_d64", "prefill_q20_d64",
-         "prefill_q30_d128"]
+         "prefill_q30_d128", "mla_h16_b1"]
 
 
 def fused_splits(d_default: int) -> int:

@@ -42,6 +42,10 @@ def small_cases():
         "mla_h4": scaled("mla_b48", context_lens=(3000, 1, 2100), num_q_heads=4, prefix_len=0, prefix_group=0,
                          seed=29),
         "gqa_d64_bf16": scaled("gqa_64k_d64", context_lens=(4100, 1, 700), seed=32),
+        # one request with 16 and 20 rows per KV head: the ring shape where a
+        # batch takes key streams
+        "mla_h16_b1": scaled("mla_b48", context_lens=(6000,), prefix_len=0, prefix_group=0, seed=40),
+        "gqa_g20_b1": scaled("gqa_64k", context_lens=(7000,), num_q_heads=40, seed=41),
         # causal prefill: every token a query row, shorter sequences right-aligned
         "prefill_small_d64": scaled("prefill_varlen_d64", context_lens=(300, 129, 64, 1), q_len=300, seed=34),
         "prefill_small_d128": scaled("prefill_2048x4_d128", context_lens=(257, 257), q_len=257, seed=35),
