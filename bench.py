@@ -253,7 +253,7 @@ def cpu_baseline(inp, kv_bytes, budget_s):
 # Configurations timed beside the headline one in the default run, each with
 # its own stage-1 roofline: the tiny fp32 check, MLA batch 48 with and
 # without shared prefixes, the 128-head MLA and the varlen drafts.
-EXTRA_CONFIGS = "gqa_tiny_f32,mla_b48,mla_b48_ctl,mla_wide,varlen_drafts"
+EXTRA_CONFIGS = "gqa_tiny_f32,mla_b48,mla_b48_ctl,mla_b1,mla_wide,varlen_drafts"
 
 
 def measure(w, args, stream, splits=0, flags=0, want_inputs=False):

@@ -13,6 +13,9 @@ Workloads that stand in for the traffic the pages measure:
 * ``mla_b48_ctl``    - the same shape with no sharing: every request owns
   68,000 private keys, so the pool exceeds 2 GiB (64-bit offsets) and logical
   KV bytes equal unique bytes.
+* ``mla_b1``         - one request of the MLA shape (68,000 keys, 16 query
+  heads): the batch-1 end of the same PR's concurrency sweep (Motivation,
+  batch-1 paragraph: at batch 1 the split count alone must fill the CUs).
 * ``mla_wide``       - the bh64-class MLA shape (128 query heads, 64 requests
   of 16,384 private keys).
 * ``varlen_drafts``  - varlen GQA with 4 causal draft tokens per request,
@@ -138,6 +141,10 @@ def _mk() -> dict:
         name="mla_b48_ctl", batch=48, q_len=1, num_q_heads=16, num_kv_heads=1,
         head_dim_qk=576, head_dim_v=512, page_size=1, kv_dtype="bf16",
         context_lens=(68000,) * 48, pool_pages=48 * 68000, v_aliases_k=True, seed=33)
+    c["mla_b1"] = Workload(
+        name="mla_b1", batch=1, q_len=1, num_q_heads=16, num_kv_heads=1,
+        head_dim_qk=576, head_dim_v=512, page_size=1, kv_dtype="bf16",
+        context_lens=(68000,), pool_pages=68000, v_aliases_k=True, seed=42)
     c["mla_wide"] = Workload(
         name="mla_wide", batch=64, q_len=1, num_q_heads=128, num_kv_heads=1,
         head_dim_qk=576, head_dim_v=512, page_size=1, kv_dtype="bf16",
