@@ -565,7 +565,7 @@ def test_stage2_alone_on_random_partials(S, Hq, dtype):
 FULL = [("gqa_64k", None), ("gqa_64k_d64", None), ("varlen_drafts", None), ("prefill_2048x4_d64", None),
         ("prefill_2048x4_d128", (0, 3)), ("prefill_varlen_d64", None), ("prefill_varlen_d128", None),
         ("mla_b48", (0, 13, 47)),
-        ("mla_wide", (0, 63)), ("mla_b48_ctl", (5, 40))]
+        ("mla_wide", (0, 63)), ("mla_b48_ctl", (5, 40)), ("mla_b1", None)]
 
 
 @pytest.mark.parametrize("name,requests", FULL)
