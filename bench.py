@@ -381,13 +381,10 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
-    from workloads import get, scaled
+    from workloads import get
 
     stream = torch.cuda.Stream()
-    w = get(args.config)
-    if args.batch:   # same requests, B of them; the page pool in proportion (at least what they take)
-        w = scaled(args.config, batch=args.batch, pool_pages=-(-w.pool_pages * args.batch // w.batch))
-        w = scaled(args.config, batch=args.batch, pool_pages=max(w.pool_pages, w.pages_needed()))
+    w = batch_workload(args.config, args.batch) if args.batch else get(args.config)
     head, inp = measure(w, args, stream, args.splits, args.flags, want_inputs=not args.no_cpu_baseline)
     kv_bytes = head["kv_bytes_per_op"]
     us_op, us_s1 = head["us_per_op"], head["stage1_us"]
@@ -447,6 +444,16 @@ def main():
                 r["read_probe"] = same
             res["configs"][name] = r
     print(json.dumps(res), flush=True)
+
+
+def batch_workload(name: str, batch: int):
+    """The named workload with `batch` requests of its first request's
+    length (the same page size, heads and sharing pattern), its page pool
+    scaled in proportion and never below the pages the tables take."""
+    from workloads import get, scaled
+    w = get(name)
+    w = scaled(name, batch=batch, pool_pages=-(-w.pool_pages * batch // w.batch))
+    return scaled(name, batch=batch, pool_pages=max(w.pool_pages, w.pages_needed()))
 
 
 def source_hash() -> str:
