@@ -272,6 +272,10 @@ def measure(w, args, stream, splits=0, flags=0, want_inputs=False):
                                      head_dim_v=w.head_dim_v, causal=w.causal)
     # the workload's lengths are known on the host (ragged batches may get
     # one fixed split length for every request)
+    # a workload without shared prefixes shares no page between requests,
+    # which the plan may be told
+    if not w.prefix_group:
+        flags |= sk.ATTN_PLAN_PRIVATE_PAGES
     plan = sk.attn_decode_plan_lens(desc, [int(x) for x in w.context_lens], splits or w.num_splits, flags)
     S = plan.num_splits
     counts = None

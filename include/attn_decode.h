@@ -90,7 +90,7 @@ enum {
   ATTN_PLAN_POLICY_P2 = 1,          /* split count = max(1, 256 / batch), the policy the
                                        aiter PR's per-lever table was measured at */
   ATTN_PLAN_NO_XCD_REMAP = 2,       /* keep the plain (split-minor) workgroup order */
-  ATTN_PLAN_FUSED_MERGE = 4         /* run merges in stage 1 when 2 <= S <= 64: the workgroup
+  ATTN_PLAN_FUSED_MERGE = 4,        /* run merges in stage 1 when 2 <= S <= 64: the workgroup
                                        that finishes a row group's last split merges the group,
                                        so no second launch waits on an idle part (aiter PR
                                        #4758, Motivation, batch-1 paragraph).  Matrix-core
@@ -99,6 +99,13 @@ enum {
                                        MI355X merging a whole group's partials on one CU
                                        (with the per-XCD L2 write-back of each release)
                                        takes longer than the launch it saves */
+  ATTN_PLAN_PRIVATE_PAGES = 8       /* performance hint: no KV page is shared between the
+                                       batch's requests.  With 16-63 query rows per KV head
+                                       the planner then takes the one-wave ring shape, which
+                                       streams private pages faster, instead of four key
+                                       streams, which compute four blocks at once and pay off
+                                       when requests re-read shared prefix pages from the L2.
+                                       Results do not depend on it (either shape is exact) */
 };
 
 /* Kernel families the planner picks from. */

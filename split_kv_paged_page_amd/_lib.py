@@ -22,6 +22,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_PLAN_POLICY_P2 = 1
 ATTN_PLAN_NO_XCD_REMAP = 2
 ATTN_PLAN_FUSED_MERGE = 4
+ATTN_PLAN_PRIVATE_PAGES = 8
 ATTN_VARIANT_VALU, ATTN_VARIANT_MFMA = 1, 2
 
 EXPORTED = ["attn_decode_plan", "attn_decode_plan_lens", "attn_decode_run", "attn_decode_partials", "attn_decode_merge",

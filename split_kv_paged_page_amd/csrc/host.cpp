@@ -315,7 +315,7 @@ attn_status plan_impl(const attn_decode_desc* desc, int32_t max_context_len, con
     return fail(ATTN_EINVAL, "max_context_len %d exceeds max_pages_per_req * page_size", max_context_len);
   if (num_splits < 0 || num_splits > kMaxSplits)
     return fail(ATTN_EINVAL, "num_splits must be in [0, %d]", kMaxSplits);
-  if (flags & ~(ATTN_PLAN_POLICY_P2 | ATTN_PLAN_NO_XCD_REMAP | ATTN_PLAN_FUSED_MERGE))
+  if (flags & ~(ATTN_PLAN_POLICY_P2 | ATTN_PLAN_NO_XCD_REMAP | ATTN_PLAN_FUSED_MERGE | ATTN_PLAN_PRIVATE_PAGES))
     return fail(ATTN_EINVAL, "unknown plan flags 0x%x", flags);
 
   const attn_decode_desc& d = *desc;
@@ -343,13 +343,14 @@ attn_status plan_impl(const attn_decode_desc* desc, int32_t max_context_len, con
   p.xcd_remap = (flags & ATTN_PLAN_NO_XCD_REMAP) || d.q_len > 1 || d.batch == 1 ? 0 : 1;
   // bf16 runs on the matrix cores at every group size (a 16-row tile part
   // empty still costs a fraction of the vector-ALU work per key); fp32 runs
-  // on the vector ALUs.  One request takes a ring shape where several would
-  // take key streams (16-63 rows): the streams' four waves compute four
-  // blocks at once but load each block only when its wave is free, which
-  // pays when many requests re-read shared prefix pages from the L2, and
-  // nothing shares pages within one request.
+  // on the vector ALUs.  One request, or a batch whose requests share no
+  // page (the caller's hint), takes a ring shape where a batch would take key
+  // streams (16-63 rows): the streams' four waves compute four blocks at once
+  // but load each block only when its wave is free, which pays when requests
+  // re-read shared prefix pages from the L2.
+  const bool streams = d.batch > 1 && !(flags & ATTN_PLAN_PRIVATE_PAGES);
   const splitkv::MfmaShape ms =
-      splitkv::stage1_mfma_shape(d.dtype, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0, rows, d.batch > 1);
+      splitkv::stage1_mfma_shape(d.dtype, d.head_dim_qk, d.head_dim_v, d.v_aliases_k != 0, rows, streams);
   int wgs_per_cu = 2;
   if (ms.rw > 0) {
     p.variant = ATTN_VARIANT_MFMA;

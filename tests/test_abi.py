@@ -144,6 +144,15 @@ def test_kernel_choice_by_rows_per_kv_head():
         p = sk.attn_decode_plan(desc(B=48, Hq=hq, **mla), 68000, 0)
         assert (p.variant, p.rows_per_wg, p.stage1_waves) == want, (hq, want)
     assert sk.attn_decode_plan(desc(B=1, Hq=16, **mla), 68000, 0).stage1_waves == 1
+    # requests that share no page (the caller's hint): the ring shape for a batch too
+    priv = sk.ATTN_PLAN_PRIVATE_PAGES
+    assert sk.attn_decode_plan(desc(B=48, Hq=16, **mla), 68000, 0, priv).stage1_waves == 1
+    assert sk.attn_decode_plan(desc(B=4, Hq=32), 4096, 0, priv).stage1_waves == 1
+    assert sk.attn_decode_plan(desc(B=4, Hq=128, Hkv=2), 4096, 0, priv).stage1_waves == 4   # 64 rows: a ring already
+    assert sk.attn_decode_plan(desc(B=4, Hq=32), 4096, 0, priv).key != sk.attn_decode_plan(desc(B=4, Hq=32), 4096, 0).key
+    with pytest.raises(sk.AttnDecodeError) as ei:      # unknown flag bits
+        sk.attn_decode_plan(desc(B=4), 4096, 0, 16)
+    assert ei.value.status == sk.ATTN_EINVAL
     assert sk.attn_decode_plan(desc(Hq=16, Dk=64, Dv=64), 4096, 0).variant == M     # bf16 head dim 64
     # causal prefill rows (query positions x group) at head dims 64 and 128: four 16-row waves sharing
     # each block from 64 rows on (eight from 128 at head dim 128), four key streams from 16
@@ -222,8 +231,8 @@ def test_fused_merge_plan_layout_and_init_checks():
     assert L.attn_decode_workspace_init(ctypes.byref(fused), None, 1 << 20, None) == sk.ATTN_EINVAL
     assert L.attn_decode_workspace_init(ctypes.byref(fused), (1 << 20) + 16, 1 << 20, None) == sk.ATTN_EINVAL
     assert L.attn_decode_workspace_init(ctypes.byref(fused), 1 << 20, counters * 4 - 4, None) == sk.ATTN_EWORKSPACE
-    with pytest.raises(sk.AttnDecodeError) as ei:
-        sk.attn_decode_plan(desc(), 4096, 8, 8)
+    with pytest.raises(sk.AttnDecodeError) as ei:      # an unknown flag bit
+        sk.attn_decode_plan(desc(), 4096, 8, 16)
     assert ei.value.status == sk.ATTN_EINVAL
 
 

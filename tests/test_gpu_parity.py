@@ -45,6 +45,8 @@ def small_cases():
         # one request with 16 and 20 rows per KV head: the ring shape where a
         # batch takes key streams
         "mla_h16_b1": scaled("mla_b48", context_lens=(6000,), prefix_len=0, prefix_group=0, seed=40),
+        "mla_h16_b4": scaled("mla_b48", context_lens=(3000, 1, 2100, 5000), prefix_len=0, prefix_group=0,
+                             seed=43),
         "gqa_g20_b1": scaled("gqa_64k", context_lens=(7000,), num_q_heads=40, seed=41),
         # causal prefill: every token a query row, shorter sequences right-aligned
         "prefill_small_d64": scaled("prefill_varlen_d64", context_lens=(300, 129, 64, 1), q_len=300, seed=34),
@@ -133,6 +135,22 @@ def test_parity_small_lens_plans(name):
     d = Decode(inp, lens=True).run()
     e_out, e_lse = check_against_oracle(d, tol_for(w))
     print(f"{name}: S={d.S} chunk={d.plan.split_chunk} out {e_out:.2e} lse {e_lse:.2e}")
+
+
+@pytest.mark.parametrize("name", ["gqa_g20_bf16", "mla_h16_b4", "gqa_g12_bf16"])
+def test_private_pages_hint(name):
+    """Plans told that requests share no page: batches of 16-63 rows per KV
+    head take the one-wave ring shape; the result is the same attention."""
+    import split_kv_paged_page_amd as sk
+    w = small_cases()[name]
+    inp = inputs(name, w)
+    d = Decode(inp, flags=sk.ATTN_PLAN_PRIVATE_PAGES)
+    rows = w.num_q_heads // w.num_kv_heads * w.q_len
+    assert d.plan.stage1_waves == 1 or rows >= 64, d.plan.stage1_waves
+    say(f"private pages {name}: B={w.batch} rows={rows} waves={d.plan.stage1_waves} run")
+    d.run()
+    e_out, e_lse = check_against_oracle(d, tol_for(w))
+    print(f"{name}: S={d.S} waves={d.plan.stage1_waves} out {e_out:.2e} lse {e_lse:.2e}")
 
 
 @pytest.mark.parametrize("name,device_lens", [
