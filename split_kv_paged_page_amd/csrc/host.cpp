@@ -356,7 +356,14 @@ attn_status plan_impl(const attn_decode_desc* desc, int32_t max_context_len, con
     p.variant = ATTN_VARIANT_MFMA;
     p.rows_per_wg = 16 * ms.rw;
     p.stage1_waves = ms.rw * ms.kw;
-    wgs_per_cu = kLdsPerCu / ms.smem < 2 ? 1 : 2;
+    // The one-wave ring at head dim 128 holds two 16 KB blocks in flight,
+    // and one such workgroup per CU walked twice the keys at the same rate
+    // with half the partials to merge: 64K GQA whole op 18.73 -> 18.25 us,
+    // and 52.3 -> 51.7 / 99.3 -> 98.0 at batch 4 / 8 (30.2 -> 30.4 at 2).
+    // At head dim 64 (8 KB blocks) one per CU was far slower (stage 1 9.96
+    // -> 12.0 us): two keep enough bytes in flight.
+    const bool one_wave_d128 = ms.rw == 1 && ms.kw == 1 && d.head_dim_qk == 128;
+    wgs_per_cu = kLdsPerCu / ms.smem < 2 || one_wave_d128 ? 1 : 2;
   } else {
     const int rt = pick_rows_per_wg(d.dtype, d.head_dim_qk, d.head_dim_v, rows);
     if (!rt)

@@ -167,8 +167,10 @@ def test_kernel_choice_by_rows_per_kv_head():
 
 def test_default_split_count_fills_one_round():
     # two workgroups per CU where the LDS allows (vector-ALU kernel, the lone
-    # matrix-core wave at head dim 128), one otherwise
-    assert sk.attn_decode_plan(desc(), 65536, 0).num_splits == 512 // 2
+    # matrix-core wave at head dim 64), one otherwise (and for the lone wave at
+    # head dim 128, whose two blocks in flight keep a CU streaming)
+    assert sk.attn_decode_plan(desc(), 65536, 0).num_splits == 256 // 2
+    assert sk.attn_decode_plan(desc(Dk=64, Dv=64), 65536, 0).num_splits == 512 // 2
     assert sk.attn_decode_plan(desc(dtype=sk.ATTN_F32), 65536, 0).num_splits == 512 // 2
     mla = dict(Hkv=1, Dk=576, Dv=512, P=1, maxp=68000, alias=1, pages=655360)
     assert sk.attn_decode_plan(desc(B=48, Hq=4, **mla), 68000, 0).num_splits == 256 // 48

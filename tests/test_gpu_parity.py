@@ -58,7 +58,7 @@ def small_cases():
         "gqa_f32_g8": scaled("gqa_64k", context_lens=(3000, 1, 777), kv_dtype="f32", seed=28),
         "gqa_f32_g16": scaled("gqa_64k", context_lens=(2100, 300), num_q_heads=32, kv_dtype="f32", seed=31),
         # ragged batches whose plans with known lengths take a fixed split
-        # length (192 keys for both)
+        # length (320 keys on the matrix cores, 192 on the vector ALUs)
         "gqa_bf16_ragged8": scaled("gqa_64k", context_lens=(9000, 100, 3000, 6000, 1, 12000, 500, 7000), seed=38),
         "gqa_f32_ragged6": scaled("gqa_64k", context_lens=(20000, 1000, 5000, 300, 12000, 7000), kv_dtype="f32",
                                   seed=39),
