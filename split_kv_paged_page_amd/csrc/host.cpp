@@ -391,8 +391,10 @@ attn_status plan_impl(const attn_decode_desc* desc, int32_t max_context_len, con
     if (S < 1) S = 1;
   } else {
     // One full round of workgroups: two per CU where the LDS allows it (VALU
-    // workgroups, the lone MFMA wave at head dim 128), else one.  A third
-    // lone wave per CU was measured slower (64K GQA: 16.3 us against 15.7).
+    // workgroups, the lone MFMA wave at head dim 64), else one (and one for
+    // the lone wave at head dim 128, above).  Three lone waves per CU at head
+    // dim 128 were slower still (64K GQA stage 1: 16.3 us against 15.7 at
+    // two, 15.3 at one).
     const int per_split = d.batch * d.num_kv_heads * p.head_tiles;
     const int target = wgs_per_cu * kNumCu;
     S = target / per_split;
