@@ -609,9 +609,14 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
         // kernel's end.  Drafts whole op 15.31 -> 14.54 us, stage 1 10.71 ->
         // 10.21; MLA batch 48 unchanged; at head dim 128 (8 KB per 64K GQA
         // workgroup) stage 1 was 0.2 us slower, so narrower rows keep plain
-        // stores.
+        // stores.  A store of more than 8 bytes still reads its data VGPRs
+        // after issue, and the compiler, which sees only assembly here, may
+        // write the next four outputs into the same registers at once: the
+        // s_nop supplies the wait state the ISA requires before that write
+        // (without it, an epilogue that reused the registers at once stored
+        // the last four lanes of every 16 wrong).
         const f32x4_t ov = {o.x, o.y, o.z, o.w};
-        asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(po), "v"(ov) : "memory");
+        asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(po), "v"(ov) : "memory");
         if (d == 0) asm volatile("global_store_dword %0, %1, off sc1" ::"v"(pl), "v"(lse) : "memory");
       } else {
         *(float4*)po = o;
