@@ -258,6 +258,67 @@ attn_status attn_decode_split_range(const attn_decode_plan_t* plan, int32_t cont
                                     int32_t* end);
 
 /*
+ * Shared-prefix plans.  aiter PR #4758's MLA workload (Test Plan, workload
+ * paragraph) has groups of 8 consecutive requests that share a 63,240-token
+ * prefix (the same page ids); its kernel leaves the sharing to the L2
+ * (Technical Details item 2: the programs of one split on one XCD).  A
+ * caller that knows the groups can instead have the shared keys scored once
+ * for all of a group's query rows.  Splits of a request's keys merged by the
+ * log-sum-exp reduction give the unsplit result (Motivation; Technical
+ * Details item 3), so splitting each row's keys into the shared ones and its
+ * own changes nothing but float rounding:
+ *   - the shared pass treats group g (requests gG .. gG + G - 1) as one
+ *     request of G * q_len query rows (its members' rows, which follow one
+ *     another in q and out) over keys [0, prefix_len), read through member
+ *     gG's page-table row, in shared.num_splits splits by the split rule;
+ *   - the own pass runs every request over keys [prefix_len, ctx[b]), in
+ *     own.num_splits splits by the split rule applied to ctx[b] - prefix_len;
+ *   - one stage-2 merge over both sets: row r's split slots are the shared
+ *     pass's splits 0 .. shared.num_splits - 1, then the own pass's.
+ * The workspace holds num_splits = shared.num_splits + own.num_splits slots
+ * per row: o_part fp32 [B, q_len, H_q, num_splits, Dv] at offset 0, then
+ * lse_part fp32 [B, q_len, H_q, num_splits] at the next multiple of 256
+ * bytes; workspace_bytes is its size (rounded up to 256).  shared is unused
+ * (all zero) when prefix_len is 0.
+ */
+typedef struct attn_decode_prefix_plan_t {
+  attn_decode_plan_t shared;  /* the groups' shared keys (virtual batch B / G, q_len G * q_len) */
+  attn_decode_plan_t own;     /* every request's keys past the prefix */
+  int32_t prefix_group;       /* G */
+  int32_t prefix_len;         /* shared keys per group */
+  int32_t num_splits;         /* split slots per row */
+  int32_t reserved;
+  int64_t workspace_bytes;
+  uint64_t key;               /* hash of both plans, G and prefix_len */
+} attn_decode_prefix_plan_t;
+
+/*
+ * Plan a shared-prefix decode.  prefix_group G >= 1 must divide batch;
+ * prefix_len must be a multiple of page_size with prefix_len + q_len - 1 <=
+ * max_context_len; flags may hold ATTN_PLAN_NO_XCD_REMAP (the own pass is
+ * always planned with ATTN_PLAN_PRIVATE_PAGES: its keys are private).
+ * ATTN_EINVAL / ATTN_EUNSUPPORTED as attn_decode_plan.  Preconditions the
+ * run cannot check: within a group the page-table rows hold the same page
+ * ids in their first prefix_len / page_size entries, and every request has
+ * ctx[b] >= prefix_len + q_len - 1 (each of its rows sees the whole prefix).
+ */
+attn_status attn_decode_plan_prefix(const attn_decode_desc* desc, int32_t max_context_len,
+                                    int32_t prefix_group, int32_t prefix_len, int32_t flags,
+                                    attn_decode_prefix_plan_t* plan);
+
+/*
+ * Run a shared-prefix plan: the shared pass (when prefix_len > 0), the own
+ * pass and the merge, enqueued on `stream` in that order.  Arguments as
+ * attn_decode_run (always with the plan's split counts); workspace_bytes must
+ * be at least plan->workspace_bytes (ATTN_EWORKSPACE otherwise).
+ */
+attn_status attn_decode_run_prefix(const attn_decode_prefix_plan_t* plan, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* page_table, const int32_t* context_lens,
+                                   float scale, void* out, float* lse, void* workspace,
+                                   int64_t workspace_bytes, void* stream);
+
+/*
  * For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
  * decode as attn_decode_run (same kernels, same bits), with the workspace

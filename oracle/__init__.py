@@ -6,9 +6,9 @@ no code with the HIP path; both take their inputs from ``workloads``.
 """
 
 from .reference import (SPLIT_ALIGN, attend, decode_reference, gather, kv_head_of,
-                        merge_reference, softmax_weights, split_bounds, split_reference,
-                        to_f64, visible_keys)
+                        merge_reference, prefix_split_bounds, softmax_weights, split_bounds,
+                        split_reference, to_f64, visible_keys)
 
 __all__ = ["SPLIT_ALIGN", "attend", "decode_reference", "gather", "kv_head_of",
-           "merge_reference", "softmax_weights", "split_bounds", "split_reference",
-           "to_f64", "visible_keys"]
+           "merge_reference", "prefix_split_bounds", "softmax_weights", "split_bounds",
+           "split_reference", "to_f64", "visible_keys"]

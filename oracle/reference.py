@@ -32,7 +32,12 @@ Readings where the pages are silent:
   imply), or with c a fixed split length shared by every request of a
   batch (a request then holds ceil(L/c) non-empty splits); a split with no
   visible key gives out = 0, lse = -inf;
-* an empty row (no visible key) gives out = 0, lse = -inf.
+* an empty row (no visible key) gives out = 0, lse = -inf;
+* shared-prefix plans (groups of requests whose first keys are the same
+  pages, as in the aiter PR's MLA workload, Test Plan): a row's splits are
+  those of its group's shared keys [0, prefix) by the split rule, then those
+  of its own keys [prefix, L) by the same rule applied to L - prefix and
+  shifted by prefix.
 """
 
 from __future__ import annotations
@@ -95,6 +100,18 @@ def split_bounds(L: int, S: int, A: int = SPLIT_ALIGN, chunk: int | None = None)
         e = min((s + 1) * chunk, max(L, 0))
         out.append((b, e))
     return out
+
+
+def prefix_split_bounds(L: int, prefix: int, S_shared: int, S_own: int, A: int = SPLIT_ALIGN) -> list:
+    """Split ranges of a request with L keys whose first ``prefix`` keys are
+    shared with its group: the S_shared splits of [0, prefix) (none when
+    prefix is 0), then the S_own splits of [prefix, L), each set by the split
+    rule of split_bounds."""
+    if prefix < 0 or prefix > max(L, 0):
+        raise ValueError("prefix must lie in [0, L]")
+    shared = split_bounds(prefix, S_shared, A) if prefix > 0 else []
+    own = [(prefix + b, prefix + e) for (b, e) in split_bounds(L - prefix, S_own, A)]
+    return shared + own
 
 
 def kv_head_of(h: int, num_q_heads: int, num_kv_heads: int) -> int:
@@ -192,9 +209,11 @@ def decode_reference(inp, requests=None) -> tuple:
     return out, lse
 
 
-def split_reference(inp, S: int, A: int = SPLIT_ALIGN, requests=None, chunk: int | None = None) -> tuple:
+def split_reference(inp, S: int, A: int = SPLIT_ALIGN, requests=None, chunk: int | None = None,
+                    bounds_of=None) -> tuple:
     """Per-split normalised partial outputs and log-sum-exps, splits as in
-    split_bounds (``chunk``: fixed split length for every request).
+    split_bounds (``chunk``: fixed split length for every request), or as
+    ``bounds_of(L)`` gives them (a list of S ranges, e.g. prefix_split_bounds).
 
     Returns (o_part [B, q_len, H_q, S, Dv], lse_part [B, q_len, H_q, S]).
     """
@@ -204,7 +223,9 @@ def split_reference(inp, S: int, A: int = SPLIT_ALIGN, requests=None, chunk: int
     lse_part = np.full((w.batch, w.q_len, w.num_q_heads, S), np.nan)
     for b in (range(w.batch) if requests is None else requests):
         L = int(inp.context_lens[b])
-        bounds = split_bounds(L, S, A, chunk)
+        bounds = split_bounds(L, S, A, chunk) if bounds_of is None else bounds_of(L)
+        if len(bounds) != S:
+            raise ValueError(f"{len(bounds)} split ranges for S = {S}")
         for kvh in range(w.num_kv_heads):
             idx, qr = _request_rows(inp, b, kvh)
             K, V = _kv(inp, b, kvh, L)

@@ -27,7 +27,7 @@ ATTN_VARIANT_VALU, ATTN_VARIANT_MFMA = 1, 2
 
 EXPORTED = ["attn_decode_plan", "attn_decode_plan_lens", "attn_decode_run", "attn_decode_partials", "attn_decode_merge",
             "attn_decode_workspace_layout", "attn_decode_workspace_init", "attn_decode_split_range",
-            "attn_decode_run_noalloc", "attn_decode_last_error"]
+            "attn_decode_run_noalloc", "attn_decode_plan_prefix", "attn_decode_run_prefix", "attn_decode_last_error"]
 NOALLOC_SCRATCH_BYTES = 64 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
 MAX_SPLIT_TABLE = 64               # ATTN_MAX_SPLIT_TABLE
 
@@ -61,6 +61,18 @@ class AttnDecodePlan(ctypes.Structure):
         d = {f: getattr(self, f) for f, _ in self._fields_ if f not in ("desc", "split_start")}
         d["split_start"] = list(self.split_start)
         d["desc"] = {f: getattr(self.desc, f) for f, _ in AttnDecodeDesc._fields_}
+        return d
+
+
+class AttnDecodePrefixPlan(ctypes.Structure):
+    _fields_ = [("shared", AttnDecodePlan), ("own", AttnDecodePlan)] + [(n, ctypes.c_int32) for n in (
+        "prefix_group", "prefix_len", "num_splits", "reserved")] + \
+        [("workspace_bytes", ctypes.c_int64), ("key", ctypes.c_uint64)]
+
+    def as_dict(self) -> dict:
+        d = {f: getattr(self, f) for f, _ in self._fields_ if f not in ("shared", "own")}
+        d["shared"] = self.shared.as_dict()
+        d["own"] = self.own.as_dict()
         return d
 
 
@@ -101,6 +113,8 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_workspace_init.argtypes = [P(AttnDecodePlan), vp, i64, vp]
         L.attn_decode_split_range.argtypes = [P(AttnDecodePlan), i32, i32, i32, P(i32), P(i32)]
         L.attn_decode_run_noalloc.argtypes = [P(AttnDecodePlan), vp, vp, vp, vp, vp, f32, i32, vp, vp, vp]
+        L.attn_decode_plan_prefix.argtypes = [P(AttnDecodeDesc), i32, i32, i32, i32, P(AttnDecodePrefixPlan)]
+        L.attn_decode_run_prefix.argtypes = [P(AttnDecodePrefixPlan), vp, vp, vp, vp, vp, f32, vp, vp, vp, i64, vp]
         L.attn_decode_last_error.argtypes = []
         L.attn_decode_last_error.restype = ctypes.c_char_p
         for n in EXPORTED[:-1]:
@@ -162,6 +176,24 @@ def attn_decode_plan_lens(desc: AttnDecodeDesc, host_context_lens, num_splits: i
     p = AttnDecodePlan()
     _check(lib().attn_decode_plan_lens(ctypes.byref(desc), arr, num_splits, flags, ctypes.byref(p)))
     return p
+
+
+def attn_decode_plan_prefix(desc: AttnDecodeDesc, max_context_len: int, prefix_group: int, prefix_len: int,
+                            flags: int = 0) -> AttnDecodePrefixPlan:
+    """Plan for batches whose groups of prefix_group consecutive requests share
+    their first prefix_len keys (the same page ids)."""
+    p = AttnDecodePrefixPlan()
+    _check(lib().attn_decode_plan_prefix(ctypes.byref(desc), max_context_len, prefix_group, prefix_len, flags,
+                                         ctypes.byref(p)))
+    return p
+
+
+def attn_decode_run_prefix(plan, q, k_cache, v_cache, page_table, context_lens, scale, out, lse, workspace,
+                           workspace_bytes=None, stream=None):
+    wb = workspace_bytes if workspace_bytes is not None else _nbytes(workspace)
+    _check(lib().attn_decode_run_prefix(ctypes.byref(plan), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(page_table), _ptr(context_lens), float(scale), _ptr(out), _ptr(lse),
+                                        _ptr(workspace), wb, _stream(stream)))
 
 
 def attn_decode_run(plan, q, k_cache, v_cache, page_table, context_lens, scale, num_splits, out,

@@ -209,13 +209,25 @@ __device__ __forceinline__ void read_stage1_start_args(const Stage1Params& p) {
                "s"(p.fd_batch.shift), "s"(p.fd_splits.mul), "s"(p.fd_splits.shift), "s"(p.fd_live.mul),
                "s"(p.fd_live.shift), "s"(p.fd_group.mul), "s"(p.fd_group.shift), "s"(p.split_chunk),
                "s"(p.align_shift), "s"(p.guess_ctx), "s"(p.rows_total), "s"(p.q_len), "s"(p.page_shift),
-               "s"(p.max_pages), "s"(p.page_table), "s"(p.ctx));
+               "s"(p.max_pages), "s"(p.page_table), "s"(p.ctx), "s"(p.key_base), "s"(p.fixed_ctx));
   // The split table's first entries (the lookup's fast path).
   asm volatile("" ::"s"(p.split_start[0]), "s"(p.split_start[1]), "s"(p.split_start[2]), "s"(p.split_start[3]),
                "s"(p.split_start[4]), "s"(p.split_start[5]), "s"(p.split_start[6]), "s"(p.split_start[7]),
                "s"(p.split_start[8]), "s"(p.split_start[9]), "s"(p.split_start[10]), "s"(p.split_start[11]),
                "s"(p.split_start[12]), "s"(p.split_start[13]), "s"(p.split_start[14]), "s"(p.split_start[15]),
                "s"(p.split_start[16]));
+}
+
+// Keys of request b this launch covers (see Stage1Params::key_base).
+__device__ __forceinline__ int launch_ctx(const Stage1Params& p, int b) {
+  if (p.fixed_ctx > 0) return p.fixed_ctx;
+  const int L = p.ctx[b] - p.key_base;
+  return L > 0 ? L : 0;
+}
+
+// Workspace slot of split s of query row `row`.
+__device__ __forceinline__ int64_t part_slot(const Stage1Params& p, int64_t row, int s) {
+  return row * p.slot_stride + p.slot_base + s;
 }
 
 // Stage-1 workgroup -> (head tile, KV head, request, split).  Without a

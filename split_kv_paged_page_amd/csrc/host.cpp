@@ -133,10 +133,21 @@ attn_status resolve_splits(const attn_decode_plan_t* p, int32_t num_splits, int*
   return ATTN_OK;
 }
 
+// One stage-1 launch of a shared-prefix plan: which keys of each request it
+// covers and where its splits go in the workspace.
+struct PassOpts {
+  int key_base = 0;      // first key (the page-table pointer moves by key_base / page_size entries)
+  int fixed_ctx = 0;     // > 0: every (virtual) request has this many keys
+  int slot_stride = 0;   // split slots per row in the workspace
+  int slot_base = 0;     // first slot of this launch
+  int pt_row_mult = 1;   // page-table rows per (virtual) request
+};
+
 attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q, const void* k,
                            const void* v, const int32_t* pt, const int32_t* ctx, float scale,
                            void* ws, int64_t ws_bytes, hipStream_t st, void* out = nullptr,
-                           float* lse_out = nullptr, void* fin_out = nullptr, float* fin_lse = nullptr) {
+                           float* lse_out = nullptr, void* fin_out = nullptr, float* fin_lse = nullptr,
+                           const PassOpts* po = nullptr) {
   const attn_decode_desc& d = plan->desc;
   if (!q || !k || !v || !pt || !ctx || !ws) return fail(ATTN_EINVAL, "a device pointer is null");
   if (d.v_aliases_k && v != k) return fail(ATTN_EINVAL, "aliased V: v_cache must equal k_cache");
@@ -149,8 +160,9 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   const float scale_log2 = scale * 1.4426950408889634f;
   if (!(scale > 0.f) || !(scale_log2 <= 3.4028234663852886e38f))
     return fail(ATTN_EINVAL, "scale must be positive and finite (got %g)", (double)scale);
+  const int slots = po ? po->slot_stride : S;
   int64_t o_off, l_off, need;
-  layout(plan, S, &o_off, &l_off, &need);
+  layout(plan, slots, &o_off, &l_off, &need);
   // Direct output (one split) leaves the workspace untouched.
   if (!out && ws_bytes < need)
     return fail(ATTN_EWORKSPACE, "workspace of %lld bytes is below the %lld needed", (long long)ws_bytes,
@@ -166,10 +178,14 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   p.q = q;
   p.k = k;
   p.v = v;
-  p.page_table = pt;
+  p.page_table = po ? pt + po->key_base / d.page_size : pt;
   p.ctx = ctx;
+  p.key_base = po ? po->key_base : 0;
+  p.fixed_ctx = po ? po->fixed_ctx : 0;
   p.o_part = (float*)((char*)ws + o_off);
   p.lse_part = (float*)((char*)ws + l_off);
+  p.slot_stride = slots;
+  p.slot_base = po ? po->slot_base : 0;
   p.scale_log2 = scale_log2;
   p.batch = d.batch;
   p.q_len = d.q_len;
@@ -179,7 +195,7 @@ attn_status enqueue_stage1(const attn_decode_plan_t* plan, int S, const void* q,
   p.page_size = d.page_size;
   p.page_shift = 0;
   while ((1 << p.page_shift) < d.page_size) ++p.page_shift;
-  p.max_pages = d.max_pages_per_req;
+  p.max_pages = d.max_pages_per_req * (po ? po->pt_row_mult : 1);
   p.causal = d.causal;
   p.num_splits = S;
   p.split_align = plan->split_align;
@@ -302,6 +318,18 @@ const char* attn_decode_last_error(void) { return g_err; }
 }  // extern "C"
 
 namespace {
+
+// The key covers every field a kernel launch depends on (rocm-libraries
+// PR #10102, Technical Details: a cache keyed on the kernel name alone
+// missed the batch baked into the binary).
+uint64_t plan_key(const attn_decode_plan_t& p) {
+  uint64_t h = fnv1a(&p.desc, sizeof(p.desc));
+  const int32_t fields[] = {p.max_context_len, p.num_splits, p.max_splits, p.split_align, p.variant,
+                            p.rows_per_wg,     p.head_tiles, p.stage1_waves, p.xcd_remap, p.flags,
+                            p.split_chunk, p.live_splits};
+  h = fnv1a(fields, sizeof(fields), h);
+  return fnv1a(p.split_start, sizeof(p.split_start), h);
+}
 
 // The planner behind attn_decode_plan and attn_decode_plan_lens; `lens`
 // (batch entries, host memory) may be null.
@@ -451,16 +479,7 @@ attn_status plan_impl(const attn_decode_desc* desc, int32_t max_context_len, con
   int64_t bytes;
   layout(&p, p.max_splits, nullptr, nullptr, &bytes);
   p.workspace_bytes = bytes;
-  // The key covers every field a kernel launch depends on (rocm-libraries
-  // PR #10102, Technical Details: a cache keyed on the kernel name alone
-  // missed the batch baked into the binary).
-  uint64_t h = fnv1a(&p.desc, sizeof(p.desc));
-  const int32_t fields[] = {p.max_context_len, p.num_splits, p.max_splits, p.split_align, p.variant,
-                            p.rows_per_wg,     p.head_tiles, p.stage1_waves, p.xcd_remap, p.flags,
-                            p.split_chunk, p.live_splits};
-  h = fnv1a(fields, sizeof(fields), h);
-  h = fnv1a(p.split_start, sizeof(p.split_start), h);
-  p.key = h;
+  p.key = plan_key(p);
   *plan = p;
   g_err[0] = 0;
   return ATTN_OK;
@@ -571,6 +590,86 @@ attn_status attn_decode_run(const attn_decode_plan_t* plan, const void* q, const
                       workspace_bytes, (hipStream_t)stream);
   if (st != ATTN_OK) return st;
   return enqueue_stage2(plan, S, workspace, workspace_bytes, out, lse, (hipStream_t)stream);
+}
+
+attn_status attn_decode_plan_prefix(const attn_decode_desc* desc, int32_t max_context_len, int32_t prefix_group,
+                                    int32_t prefix_len, int32_t flags, attn_decode_prefix_plan_t* plan) {
+  if (!plan) return fail(ATTN_EINVAL, "plan is null");
+  attn_status st = check_desc(desc);
+  if (st != ATTN_OK) return st;
+  const attn_decode_desc& d = *desc;
+  if (prefix_group < 1 || d.batch % prefix_group)
+    return fail(ATTN_EINVAL, "prefix_group must be >= 1 and divide batch %d (got %d)", d.batch, prefix_group);
+  if ((int64_t)d.max_pages_per_req * prefix_group > 0x7fffffff || (int64_t)d.q_len * prefix_group > 0x7fffffff)
+    return fail(ATTN_EINVAL, "prefix_group %d too large for the page-table rows", prefix_group);
+  if (prefix_len < 0 || prefix_len % d.page_size)
+    return fail(ATTN_EINVAL, "prefix_len must be a non-negative multiple of page_size (got %d)", prefix_len);
+  if ((int64_t)prefix_len + d.q_len - 1 > max_context_len)
+    return fail(ATTN_EINVAL, "prefix_len + q_len - 1 (%lld) exceeds max_context_len %d",
+                (long long)prefix_len + d.q_len - 1, max_context_len);
+  if (flags & ~(ATTN_PLAN_NO_XCD_REMAP | ATTN_PLAN_PRIVATE_PAGES))
+    return fail(ATTN_EINVAL, "unknown or unsupported plan flags 0x%x for a shared-prefix plan", flags);
+  attn_decode_prefix_plan_t pp{};
+  pp.prefix_group = prefix_group;
+  pp.prefix_len = prefix_len;
+  if (prefix_len > 0) {
+    // The groups' shared keys: group g is one request whose q_len * G rows
+    // are its members' rows (consecutive in q and out), all of which see
+    // every shared key.  Every such request has exactly prefix_len keys, so
+    // the XCD-contiguous order suits it whatever q_len is: the head tiles of
+    // one (group, split) then read each block on the same XCD.
+    attn_decode_desc sd = d;
+    sd.batch = d.batch / prefix_group;
+    sd.q_len = d.q_len * prefix_group;
+    sd.causal = 0;
+    st = plan_impl(&sd, prefix_len, nullptr, 0, flags & ATTN_PLAN_NO_XCD_REMAP, &pp.shared);
+    if (st != ATTN_OK) return st;
+    pp.shared.xcd_remap = (flags & ATTN_PLAN_NO_XCD_REMAP) || sd.batch == 1 ? 0 : 1;
+    pp.shared.key = plan_key(pp.shared);
+  }
+  // Every request's own keys, which no other request reads.
+  st = plan_impl(&d, max_context_len - prefix_len, nullptr, 0,
+                 (flags & ATTN_PLAN_NO_XCD_REMAP) | ATTN_PLAN_PRIVATE_PAGES, &pp.own);
+  if (st != ATTN_OK) return st;
+  pp.num_splits = pp.shared.num_splits + pp.own.num_splits;
+  int64_t bytes;
+  layout(&pp.own, pp.num_splits, nullptr, nullptr, &bytes);
+  pp.workspace_bytes = bytes;
+  const uint64_t parts[] = {pp.shared.key, pp.own.key, (uint64_t)prefix_group, (uint64_t)prefix_len};
+  pp.key = fnv1a(parts, sizeof(parts));
+  *plan = pp;
+  g_err[0] = 0;
+  return ATTN_OK;
+}
+
+attn_status attn_decode_run_prefix(const attn_decode_prefix_plan_t* plan, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* page_table, const int32_t* context_lens,
+                                   float scale, void* out, float* lse, void* workspace, int64_t workspace_bytes,
+                                   void* stream) {
+  if (!plan) return fail(ATTN_EINVAL, "plan is null");
+  if (!out) return fail(ATTN_EINVAL, "out is null");
+  if ((uintptr_t)out % 16 || (uintptr_t)lse % 4) return fail(ATTN_EINVAL, "out must be 16-byte aligned");
+  const int S = plan->num_splits, Sp = plan->prefix_len > 0 ? plan->shared.num_splits : 0;
+  if (S != Sp + plan->own.num_splits || S < 1) return fail(ATTN_EINVAL, "inconsistent shared-prefix plan");
+  hipStream_t st_ = (hipStream_t)stream;
+  attn_status st;
+  if (Sp > 0) {
+    PassOpts po;
+    po.fixed_ctx = plan->prefix_len;
+    po.slot_stride = S;
+    po.pt_row_mult = plan->prefix_group;
+    st = enqueue_stage1(&plan->shared, Sp, q, k_cache, v_cache, page_table, context_lens, scale, workspace,
+                        workspace_bytes, st_, nullptr, nullptr, nullptr, nullptr, &po);
+    if (st != ATTN_OK) return st;
+  }
+  PassOpts po;
+  po.key_base = plan->prefix_len;
+  po.slot_stride = S;
+  po.slot_base = Sp;
+  st = enqueue_stage1(&plan->own, plan->own.num_splits, q, k_cache, v_cache, page_table, context_lens, scale,
+                      workspace, workspace_bytes, st_, nullptr, nullptr, nullptr, nullptr, &po);
+  if (st != ATTN_OK) return st;
+  return enqueue_stage2(&plan->own, S, workspace, workspace_bytes, out, lse, st_);
 }
 
 attn_status attn_decode_run_noalloc(const attn_decode_plan_t* plan, const void* q, const void* k_cache,

@@ -33,6 +33,11 @@ struct Stage1Params {
   int32_t page_size, max_pages, split_align;
   const int32_t* page_table;
   const int32_t* ctx;
+  // A launch may cover part of each request's keys (shared-prefix plans):
+  // request b's keys here are ctx[b] - key_base, from key_base on (the
+  // page-table pointer already points past the first key_base / page_size
+  // entries), or fixed_ctx > 0 keys for every request.
+  int32_t key_base, fixed_ctx;
   // Split table (live_splits > 0): request b owns work items
   // [split_start[b], split_start[b+1]).
   int32_t split_start[ATTN_MAX_SPLIT_TABLE + 1];
@@ -42,8 +47,10 @@ struct Stage1Params {
   const void* v;
   int64_t ks_page, ks_head, ks_tok;   // elements
   int64_t vs_page, vs_head, vs_tok;
-  float* o_part;          // [B, q_len, Hq, S, Dv]
-  float* lse_part;        // [B, q_len, Hq, S]
+  float* o_part;          // [B, q_len, Hq, slot_stride, Dv]
+  float* lse_part;        // [B, q_len, Hq, slot_stride]
+  int32_t slot_stride;    // split slots per row in the workspace (num_splits unless the plan has several launches)
+  int32_t slot_base;      // this launch's split s goes to slot slot_base + s
   // Single split: write the final output (q dtype) and log-sum-exp directly
   // instead of partials (identical bits to merging one split).
   void* out;              // null: write partials

@@ -238,7 +238,7 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
     }
   }
 
-  const int L = p.ctx[b];
+  const int L = launch_ctx(p, b);
   int sb, se, end_max;
   bounds(L, sb, se, end_max);
   const bool guess_ok = em_g > sb_g && sb_g == sb && em_g == end_max;
@@ -600,8 +600,8 @@ __global__ __launch_bounds__(64 * RW * KW) void stage1_mfma_kernel(Stage1Params 
       store_out4(p.out, 1, row * DV + d, o);
       if (d == 0 && p.lse_out) p.lse_out[row] = lse;
     } else {
-      float* const po = p.o_part + (row * p.num_splits + s) * DV + d;
-      float* const pl = p.lse_part + row * p.num_splits + s;
+      float* const po = p.o_part + part_slot(p, row, s) * DV + d;
+      float* const pl = p.lse_part + part_slot(p, row, s);
       if constexpr (DV >= 256) {
         // Wide rows (32 KB of partials per drafts workgroup, 32 KB per MLA
         // one): write through the L2 (device-scope stores), so that the

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
   const int tile = p.causal ? p.head_tiles - 1 - wc.tile : wc.tile;
   const int kvh = wc.kvh, b = wc.b, s = wc.s;
 
-  const int L = p.ctx[b];
+  const int L = launch_ctx(p, b);
   int sb, se;
   split_range(L, p.num_splits, p.fd_splits, p.align_shift, p.split_chunk, s, sb, se);
 
@@ -328,8 +328,8 @@ __global__ __launch_bounds__(64 * NW) void stage1_valu_kernel(Stage1Params p) {
       store_out4(p.out, 0, row * DV + d, o);
       if (d == 0 && p.lse_out) p.lse_out[row] = lse;
     } else {
-      *(float4*)(p.o_part + (row * p.num_splits + s) * DV + d) = o;
-      if (d == 0) p.lse_part[row * p.num_splits + s] = lse;
+      *(float4*)(p.o_part + part_slot(p, row, s) * DV + d) = o;
+      if (d == 0) p.lse_part[part_slot(p, row, s)] = lse;
     }
   }
 }

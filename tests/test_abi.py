@@ -42,8 +42,12 @@ def test_library_exports_every_declared_function():
 def test_struct_layout_matches_header(tmp_path):
     fields_d = [f for f, _ in sk.AttnDecodeDesc._fields_]
     fields_p = [f for f, _ in sk.AttnDecodePlan._fields_]
+    fields_pp = [f for f, _ in sk.AttnDecodePrefixPlan._fields_]
     src = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void){",
-           'printf("%zu %zu\\n", sizeof(attn_decode_desc), sizeof(attn_decode_plan_t));']
+           'printf("%zu %zu %zu\\n", sizeof(attn_decode_desc), sizeof(attn_decode_plan_t), '
+           'sizeof(attn_decode_prefix_plan_t));']
+    for f in fields_pp:
+        src.append(f'printf("x {f} %zu\\n", offsetof(attn_decode_prefix_plan_t, {f}));')
     for f in fields_d:
         src.append(f'printf("d {f} %zu\\n", offsetof(attn_decode_desc, {f}));')
     for f in fields_p:
@@ -54,13 +58,14 @@ def test_struct_layout_matches_header(tmp_path):
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", str(c), "-o", str(exe)], check=True)
     lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
-    sd, sp = map(int, lines[0].split())
+    sd, sp, spp = map(int, lines[0].split())
     assert sd == ctypes.sizeof(sk.AttnDecodeDesc) and sp == ctypes.sizeof(sk.AttnDecodePlan)
+    assert spp == ctypes.sizeof(sk.AttnDecodePrefixPlan)
     for ln in lines[1:]:
         if not ln:
             continue
         kind, f, off = ln.split()
-        cls = sk.AttnDecodeDesc if kind == "d" else sk.AttnDecodePlan
+        cls = {"d": sk.AttnDecodeDesc, "p": sk.AttnDecodePlan, "x": sk.AttnDecodePrefixPlan}[kind]
         assert getattr(cls, f).offset == int(off), (kind, f)
 
 
@@ -308,6 +313,78 @@ def test_run_argument_errors_before_any_launch():
                 else:
                     call(*args, fake, 1 << 30, stream=0)
             assert ei.value.status == sk.ATTN_EINVAL, bad
+
+
+def test_prefix_plan_passes_and_split_rule():
+    """MLA batch 48 with 8-request groups sharing 63,240 keys: the shared pass
+    is one 128-row request per group (two 64-row head tiles) over the prefix,
+    the own pass every request over its private keys with the private-pages
+    hint; the row's slots are the shared splits then the own ones, by the
+    oracle's shared-prefix split rule."""
+    d = mla_desc(48)
+    pp = sk.attn_decode_plan_prefix(d, 68000, 8, 63240)
+    sh, own = pp.shared, pp.own
+    assert (sh.desc.batch, sh.desc.q_len, sh.desc.causal) == (6, 8, 0)
+    assert sh.max_context_len == 63240 and own.max_context_len == 68000 - 63240
+    assert sh.variant == sk.ATTN_VARIANT_MFMA and sh.rows_per_wg * sh.head_tiles >= 128
+    assert sh.xcd_remap == 1
+    assert own.flags & sk.ATTN_PLAN_PRIVATE_PAGES
+    assert pp.num_splits == sh.num_splits + own.num_splits
+    # one round of workgroups in each pass
+    assert 0 < 6 * sh.head_tiles * sh.num_splits <= 512
+    assert 0 < 48 * own.head_tiles * own.num_splits <= 512
+    al = lambda x: -(-x // 256) * 256
+    rows, S = 48 * 16, pp.num_splits
+    assert pp.workspace_bytes == al(rows * S * 512 * 4) + al(rows * S * 4)
+    for L in (63240, 63241, 64000, 68000):
+        got = [sk.attn_decode_split_range(sh, 63240, sh.num_splits, s) for s in range(sh.num_splits)]
+        got += [tuple(63240 + x for x in sk.attn_decode_split_range(own, L - 63240, own.num_splits, s))
+                for s in range(own.num_splits)]
+        assert got == oracle.prefix_split_bounds(L, 63240, sh.num_splits, own.num_splits)
+    # keys differ with the grouping and the prefix
+    assert sk.attn_decode_plan_prefix(d, 68000, 8, 63000).key != pp.key
+    assert sk.attn_decode_plan_prefix(d, 68000, 4, 63240).key != pp.key
+    # no prefix: the own pass alone
+    p0 = sk.attn_decode_plan_prefix(d, 68000, 8, 0)
+    assert p0.shared.num_splits == 0 and p0.num_splits == p0.own.num_splits
+
+
+@pytest.mark.parametrize("args,status", [
+    ((7, 100), sk.ATTN_EINVAL),        # group does not divide the batch
+    ((0, 100), sk.ATTN_EINVAL),
+    ((8, -16), sk.ATTN_EINVAL),
+    ((8, 100), sk.ATTN_EINVAL),        # not a whole number of 16-key pages
+    ((8, 1 << 20), sk.ATTN_EINVAL),    # longer than the longest context
+])
+def test_prefix_plan_rejects(args, status):
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_plan_prefix(desc(B=16), 65536, *args)
+    assert ei.value.status == status
+
+
+def test_prefix_plan_flags_and_run_errors():
+    d = desc(B=16, Hq=16, Hkv=1, Dk=576, Dv=512, P=1, maxp=68000, alias=1, pages=655360)
+    for bad in (sk.ATTN_PLAN_FUSED_MERGE, sk.ATTN_PLAN_POLICY_P2, 16):
+        with pytest.raises(sk.AttnDecodeError) as ei:
+            sk.attn_decode_plan_prefix(d, 1000, 8, 600, bad)
+        assert ei.value.status == sk.ATTN_EINVAL
+    assert sk.attn_decode_plan_prefix(d, 1000, 8, 600, sk.ATTN_PLAN_NO_XCD_REMAP).shared.xcd_remap == 0
+    # causal rows: every row must see the whole prefix
+    dc = desc(B=4, q_len=4, Hq=32, Hkv=4, Dk=256, Dv=256, causal=1)
+    sk.attn_decode_plan_prefix(dc, 2048, 2, 2032)   # 2032 + 4 - 1 <= 2048
+    with pytest.raises(sk.AttnDecodeError):
+        sk.attn_decode_plan_prefix(dc, 2048, 2, 2048)
+    pp = sk.attn_decode_plan_prefix(d, 1000, 8, 600)
+    fake = 1 << 20
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_run_prefix(pp, fake, fake, fake, fake, fake, 0.1, fake, None, fake, 16, stream=0)
+    assert ei.value.status == sk.ATTN_EWORKSPACE
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_run_prefix(pp, None, fake, fake, fake, fake, 0.1, fake, None, fake, 1 << 30, stream=0)
+    assert ei.value.status == sk.ATTN_EINVAL
+    with pytest.raises(sk.AttnDecodeError) as ei:
+        sk.attn_decode_run_prefix(pp, fake, fake, fake, fake, fake, 0.1, None, None, fake, 1 << 30, stream=0)
+    assert ei.value.status == sk.ATTN_EINVAL
 
 
 def test_noalloc_rejects_plans_beyond_its_scratch_before_any_hip_call():

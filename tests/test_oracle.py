@@ -8,7 +8,8 @@
   unsplit result for any split count, a physical page permutation leaves the
   result bitwise unchanged;
 * the split rule against the trip counts printed in aiter PR #4758's Test
-  Result tables, and against a brute-force search;
+  Result tables, and against a brute-force search (also the shared-prefix
+  split rule, whose partials must merge to the unsplit result);
 * planted mistakes (wrong slot, dropped scale, top-left causal alignment,
   wrong GQA head map, interleaved KV-head rule, V read from K, flipped merge
   sign, log base 2) each fail one of the pins above.
@@ -350,6 +351,48 @@ def test_fixed_chunk_split_merge_reproduces_unsplit():
                 assert np.max(np.abs(mo2 - o)) > 1e-6
 
 
+def test_prefix_split_rule_bruteforce():
+    """Shared-prefix splits: the shared set is the split rule over [0, prefix)
+    (found by search, as above), the own set the rule over the L - prefix
+    remaining keys, shifted by prefix; together they partition [0, L) in
+    order.  With prefix = 0 only the own set remains and equals split_bounds."""
+    def rule(n, S, A):
+        c = A
+        while S * c < n:
+            c += A
+        return [(min(s * c, n), min((s + 1) * c, n)) for s in range(S)]
+    for L in range(0, 90, 3):
+        for prefix in sorted({0, 1, L // 3, L // 2, L}):
+            if prefix > L:
+                continue
+            for Ss in (1, 2, 5):
+                for So in (1, 3, 4):
+                    for A in (1, 16, 64):
+                        got = oracle.prefix_split_bounds(L, prefix, Ss, So, A)
+                        shared = rule(prefix, Ss, A) if prefix > 0 else []
+                        own = [(prefix + b, prefix + e) for b, e in rule(L - prefix, So, A)]
+                        assert got == shared + own, (L, prefix, Ss, So, A)
+                        covered = [t for b, e in got for t in range(b, e)]
+                        assert covered == list(range(L))
+        assert oracle.prefix_split_bounds(L, 0, 4, 5) == oracle.split_bounds(L, 5)
+
+
+def test_prefix_split_merge_reproduces_unsplit():
+    # partials over the shared keys and each request's own keys merge to the
+    # unsplit result (ragged batch, causal drafts, GQA and aliased V)
+    for case in (CASES[3], CASES[4], dict(B=3, Hq=8, Hkv=2, Dk=32, Dv=32, P=1, ctx=(9, 7, 20))):
+        w = _wl(**case)
+        inp, *_ = dense_problem(w, seed=17)
+        o, l = oracle.decode_reference(inp)
+        lo = min(w.context_lens) - w.q_len + 1
+        for prefix in sorted({0, 1, max(0, lo // 2), max(0, lo)}):
+            for Ss, So in ((1, 1), (2, 3), (3, 2)):
+                op, lp = oracle.split_reference(inp, (Ss if prefix else 0) + So,
+                                                bounds_of=lambda L: oracle.prefix_split_bounds(L, prefix, Ss, So))
+                mo, ml = oracle.merge_reference(op, lp)
+                assert np.max(np.abs(mo - o)) <= 1e-12 and np.max(np.abs(ml - l)) <= 1e-12, (case, prefix)
+
+
 def test_visible_keys_rule():
     assert oracle.visible_keys(10, 1, 0, True) == 10
     assert [oracle.visible_keys(10, 4, j, True) for j in range(4)] == [7, 8, 9, 10]
@@ -413,6 +456,19 @@ def test_planted_v_from_k(monkeypatch):
         return K, K[:, :w.head_dim_v]
     _planted(monkeypatch, "_kv", bad_kv)
     assert bruteforce_error(CASES[0]) > 1e-3
+
+
+def test_planted_unshifted_own_splits(monkeypatch):
+    # own splits left at [0, L - prefix): keys overlap the shared set and the
+    # last prefix keys are never read
+    def bad(L, prefix, Ss, So, A=oracle.SPLIT_ALIGN):
+        shared = oracle.split_bounds(prefix, Ss, A) if prefix > 0 else []
+        return shared + oracle.split_bounds(L - prefix, So, A)
+    monkeypatch.setattr(oracle, "prefix_split_bounds", bad)
+    with pytest.raises(AssertionError):
+        test_prefix_split_rule_bruteforce()
+    with pytest.raises(AssertionError):
+        test_prefix_split_merge_reproduces_unsplit()
 
 
 def test_planted_merge_sign():
