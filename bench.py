@@ -20,6 +20,9 @@ batch 48 with and without shared prefixes, the 128-head MLA and the varlen
 drafts, each under "configs" with its whole-op and stage-1 times, its own
 stage-1 roofline entry, a plain cold read of the same KV bytes (unique bytes
 where prefixes are shared) and, for shared prefixes, the unique-bytes rate.
+"mla_b48+prefix" is MLA batch 48 again through the shared-prefix plan
+(attn_decode_plan_prefix: each group's shared keys scored once for all its
+members' rows), whole op only; --prefix times only that for --config.
 
 Beside stage 1 the line carries a plain device-memory read timed the same
 way (libsplitkv_probe.so): a 2 GiB streaming read, the part's practical read
@@ -67,6 +70,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step eagerly instead of from a captured graph (counter runs)")
+    ap.add_argument("--prefix", action="store_true",
+                    help="time the workload through the shared-prefix plan (whole op only)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 20 device-to-device copies of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -253,7 +258,8 @@ def cpu_baseline(inp, kv_bytes, budget_s):
 # Configurations timed beside the headline one in the default run, each with
 # its own stage-1 roofline: the tiny fp32 check, MLA batch 48 with and
 # without shared prefixes, the 128-head MLA and the varlen drafts.
-EXTRA_CONFIGS = "gqa_tiny_f32,mla_b48,mla_b48_ctl,mla_b1,mla_wide,varlen_drafts"
+EXTRA_CONFIGS = "gqa_tiny_f32,mla_b48,mla_b48+prefix,mla_b48_ctl,mla_b1,mla_wide,varlen_drafts"
+PREFIX_SUFFIX = "+prefix"   # an --extra entry <workload>+prefix: that workload through the shared-prefix plan
 
 
 def measure(w, args, stream, splits=0, flags=0, want_inputs=False):
@@ -374,6 +380,64 @@ def measure(w, args, stream, splits=0, flags=0, want_inputs=False):
     return res, (inp if want_inputs else None)
 
 
+def measure_prefix(w, args, stream):
+    """The workload through the shared-prefix plan (its groups of
+    w.prefix_group requests share their first w.prefix_len keys): the whole op
+    (shared pass, own pass, merge) as graph replays over cold KV."""
+    import torch
+
+    import split_kv_paged_page_amd as sk
+    from workloads import generate
+    from workloads.torch_io import upload
+
+    inp = generate(w)
+    t = upload(inp, "cuda")
+    desc = sk.make_desc_from_tensors(t["q"], t["k_cache"], t["v_cache"], t["page_table"],
+                                     head_dim_v=w.head_dim_v, causal=w.causal)
+    plan = sk.attn_decode_plan_prefix(desc, int(max(w.context_lens)), w.prefix_group, w.prefix_len)
+    kv_bytes, touched = w.logical_kv_bytes(), w.unique_kv_bytes()
+    R = args.replicas or max(1, -(-(1 << 30) // touched))
+    ks = [t["k_cache"]] + [t["k_cache"].clone() for _ in range(R - 1)]
+    vs = [t["v_cache"]] + [t["v_cache"].clone() for _ in range(R - 1)] if t["v_cache"] is not None else ks
+    dt = torch.float32 if w.kv_dtype == "f32" else torch.bfloat16
+    out = torch.empty((w.batch, w.q_len, w.num_q_heads, w.head_dim_v), dtype=dt, device="cuda")
+    lse = torch.empty((w.batch, w.q_len, w.num_q_heads), dtype=torch.float32, device="cuda")
+    ws = torch.empty(plan.workspace_bytes // 4, dtype=torch.float32, device="cuda")
+    scale = float(inp.scale)
+
+    def step(i):
+        r = i % R
+        sk.attn_decode_run_prefix(plan, t["q"], ks[r], vs[r], t["page_table"], t["context_lens"], scale,
+                                  out, lse, ws, stream=stream.cuda_stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+    timer = time_eager if args.eager else time_graph
+    ms, g, op_rounds = timer(step, args.steps, stream)
+    del g, ks, vs, t, out, lse, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    us_op = ms * 1e3 / args.steps
+    kv_gbs = kv_bytes / (us_op * 1e-6) / 1e9
+    return {
+        "workload": w.name, "plan": "shared prefix (attn_decode_plan_prefix)",
+        "us_per_op": round(us_op, 3),
+        "us_per_op_rounds": [round(x * 1e3 / args.steps, 3) for x in op_rounds],
+        "kv_gbs": round(kv_gbs, 1), "kv_hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
+        "unique_kv_bytes_per_op": touched,
+        "unique_kv_gbs": round(touched / (us_op * 1e-6) / 1e9, 1),
+        "unique_kv_frac": round(touched / (us_op * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "tflops_per_s": round(algorithmic_flops(w) / (us_op * 1e-6) / 1e12, 2),
+        "prefix_group": w.prefix_group, "prefix_len": w.prefix_len,
+        "shared_splits": plan.shared.num_splits if w.prefix_len else 0, "own_splits": plan.own.num_splits,
+        "shared_rows_per_wg": plan.shared.rows_per_wg, "shared_head_tiles": plan.shared.head_tiles,
+        "own_rows_per_wg": plan.own.rows_per_wg, "replicas": R, "kv_bytes_per_op": kv_bytes,
+        "plan_key": str(plan.key),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -389,6 +453,12 @@ def main():
 
     stream = torch.cuda.Stream()
     w = batch_workload(args.config, args.batch) if args.batch else get(args.config)
+    if args.prefix:   # only the shared-prefix plan's op time, one JSON object
+        if not w.prefix_group:
+            print(f"bench.py: {w.name} has no shared prefixes", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(measure_prefix(w, args, stream)), flush=True)
+        return
     head, inp = measure(w, args, stream, args.splits, args.flags, want_inputs=not args.no_cpu_baseline)
     kv_bytes = head["kv_bytes_per_op"]
     us_op, us_s1 = head["us_per_op"], head["stage1_us"]
@@ -438,6 +508,9 @@ def main():
         res["configs"] = {}
         for name in extra:
             print(f"[bench] {name}", file=sys.stderr, flush=True)
+            if name.endswith(PREFIX_SUFFIX):   # the named workload through the shared-prefix plan
+                res["configs"][name] = measure_prefix(get(name[:-len(PREFIX_SUFFIX)]), args, stream)
+                continue
             r, _ = measure(get(name), args, stream)
             if not args.no_read_probe:
                 # a plain cold read of the same KV bytes (unique bytes where
