@@ -394,7 +394,11 @@ def measure_prefix(w, args, stream):
     t = upload(inp, "cuda")
     desc = sk.make_desc_from_tensors(t["q"], t["k_cache"], t["v_cache"], t["page_table"],
                                      head_dim_v=w.head_dim_v, causal=w.causal)
-    plan = sk.attn_decode_plan_prefix(desc, int(max(w.context_lens)), w.prefix_group, w.prefix_len)
+    # a batch that is not a whole number of groups (the sweep's B < 8) forms
+    # groups of gcd(B, G) requests, which all share the prefix
+    import math
+    G = math.gcd(w.batch, w.prefix_group)
+    plan = sk.attn_decode_plan_prefix(desc, int(max(w.context_lens)), G, w.prefix_len)
     kv_bytes, touched = w.logical_kv_bytes(), w.unique_kv_bytes()
     R = args.replicas or max(1, -(-(1 << 30) // touched))
     ks = [t["k_cache"]] + [t["k_cache"].clone() for _ in range(R - 1)]
@@ -430,7 +434,7 @@ def measure_prefix(w, args, stream):
         "unique_kv_gbs": round(touched / (us_op * 1e-6) / 1e9, 1),
         "unique_kv_frac": round(touched / (us_op * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "tflops_per_s": round(algorithmic_flops(w) / (us_op * 1e-6) / 1e12, 2),
-        "prefix_group": w.prefix_group, "prefix_len": w.prefix_len,
+        "prefix_group": G, "prefix_len": w.prefix_len,
         "shared_splits": plan.shared.num_splits if w.prefix_len else 0, "own_splits": plan.own.num_splits,
         "shared_rows_per_wg": plan.shared.rows_per_wg, "shared_head_tiles": plan.shared.head_tiles,
         "own_rows_per_wg": plan.own.rows_per_wg, "replicas": R, "kv_bytes_per_op": kv_bytes,
