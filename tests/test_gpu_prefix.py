@@ -203,3 +203,40 @@ def test_prefix_full_size_mla_b48_sampled():
     d = PrefixDecode(inp).run()
     say(f"prefix mla_b48 S = {d.Sp} + {d.So}")
     check(d, requests=(0, 9, 47))
+
+
+@pytest.mark.parametrize("name", ["mla_b16_p700", "gqa_b4_g2"])
+def test_prefix_graph_replays_match_eager(name):
+    """attn_decode_run_prefix allocates nothing and never synchronises: its
+    three launches captured in a graph give the eager bits on every replay,
+    with eager work and synchronisations between replays."""
+    import torch
+    d = PrefixDecode(inputs(name)).run()
+    e_out, e_lse = d.out.clone(), d.lse.clone()
+    e_ws = d.ws.clone()
+    t = d.t
+    v = t["k_cache"] if t["v_cache"] is None else t["v_cache"]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        sk.attn_decode_run_prefix(d.plan, t["q"], t["k_cache"], v, t["page_table"], t["context_lens"],
+                                  float(d.inp.scale), d.out, d.lse, d.ws, stream=s.cuda_stream)
+    for r in range(3):
+        d.ws.fill_(float("nan"))          # eager work between replays
+        d.out.fill_(float("nan"))
+        d.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"prefix graph {name} replay {r}")
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.out.view(torch.int16), e_out.view(torch.int16)), r
+        assert torch.equal(d.lse.view(torch.int32), e_lse.view(torch.int32)), r
+        w = d.inp.w
+        rows = w.batch * w.q_len * w.num_q_heads
+        n_o = rows * d.S * w.head_dim_v
+        l_off = -(-n_o * 4 // 256) * 256 // 4
+        assert torch.equal(d.ws[:n_o].view(torch.int32), e_ws[:n_o].view(torch.int32)), r
+        assert torch.equal(d.ws[l_off:l_off + rows * d.S].view(torch.int32),
+                           e_ws[l_off:l_off + rows * d.S].view(torch.int32)), r
