@@ -75,6 +75,8 @@ struct MCfg {
   // Measured against 4 tiles: lone wave (64K GQA) 15.7 / 16.4 us, drafts
   // 13.6 / 14.4, prefill 4 x 2048 at head dim 128 139 / 162 (the smaller
   // ring also lets a third workgroup onto the CU), wide MLA 379 / 380.
+  // Again for the lone wave at head dim 128 with one workgroup per CU:
+  // 2 / 3 / 4 / 5 tiles, stage 1 18.6 / 15.4 / 15.9 / 16.3 us.
   // The four-wave shape at head dim 128 (prefill, whose keys mostly come
   // from cache) takes 2 tiles, which fits a fourth workgroup per CU: whole
   // op 4 x 2048 132.3 -> 128.0 us, varlen 95.0 -> 90.8.
