@@ -85,6 +85,8 @@ def cases():
         # causal draft rows: every row sees the whole shared part
         "drafts_g3": scaled("varlen_drafts", context_lens=(600, 700, 1000, 800, 900, 2048), prefix_group=3,
                             prefix_len=512, seed=66),
+        # every request exactly the shared keys: the own pass finds none
+        "mla_b16_all_shared": scaled("mla_b48", batch=16, context_lens=(700,) * 16, prefix_len=700, seed=68),
         # prefix 0: the own pass alone over every key
         "gqa_b4_p0": scaled("gqa_64k", context_lens=(3000, 1500, 1025, 5000), prefix_group=2, prefix_len=0,
                             seed=67),
