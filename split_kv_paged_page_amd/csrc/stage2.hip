@@ -11,12 +11,17 @@
 // No LDS and no barriers: a merge of up to 16 * LP splits is one memory
 // round trip plus a few cross-lane steps.
 //
-// LP is the smallest power of two that keeps a lane at 16 splits or fewer,
-// doubled while the merge would have fewer than 128 waves.  The split count
+// LP is the smallest power of two that keeps a lane at 16 splits or fewer
+// (8 when there are at most 16), doubled while the merge would have fewer
+// than 128 waves.  The split count
 // and the output size alone pick it, so one plan always merges in the same
 // order (same bits on every run).  Measured on the 64K GQA merge (512 pairs,
 // 256 splits): 16 lanes in 128 one-wave workgroups 3.0 us per op; the same
 // in 256-thread workgroups 4.2; 8 lanes 3.8; 32 lanes 3.5; 64 lanes 4.7.
+// At 8 rather than 16 splits per lane the drafts' merge (up to 16 splits
+// per row) takes 2 lanes: whole op 14.64 -> 14.45 us (at 4, 14.84); one
+// MLA request's 213 splits at 8 per lane (32 lanes) took 26.7 us per op
+// against 24.9 at 16 (16 lanes).
 #include "device_common.h"
 #include "launch.h"
 
@@ -26,6 +31,7 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kPer = 16;        // splits per lane held in registers per pass
+constexpr int kFewSplits = 16;  // up to this many splits, a lane takes at most half of them
 constexpr int kMinWaves = 128;  // below this, more lanes per pair
 
 template <int LP>
@@ -171,7 +177,8 @@ hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t st) {
 
 int stage2_lanes(int64_t pairs, int num_splits) {
   int lp = 1;
-  while (lp < 64 && (int64_t)lp * kPer < num_splits) lp *= 2;
+  const int per = num_splits <= kFewSplits ? kPer / 2 : kPer;
+  while (lp < 64 && (int64_t)lp * per < num_splits) lp *= 2;
   while (lp < 64 && pairs * lp < (int64_t)kMinWaves * 64) lp *= 2;
   return lp;
 }

@@ -534,17 +534,18 @@ def test_stage2_alone_on_oracle_partials(name, S):
     assert lse_err(d.lse_f64(), ml) <= 1e-5
 
 
-@pytest.mark.parametrize("S,Hq,dtype", [(S, Hq, "bf16") for S in (2, 16, 17, 256, 257, 700) for Hq in (2, 4, 16)] +
+@pytest.mark.parametrize("S,Hq,dtype", [(S, Hq, "bf16") for S in (2, 8, 9, 16, 17, 256, 257, 700) for Hq in (2, 4, 16)] +
                          [(S, 128, "bf16") for S in (2, 16, 17, 40, 100)] +
-                         [(S, 16, "f32") for S in (16, 17, 700)])
+                         [(S, 16, "f32") for S in (16, 17, 700)] + [(2000, 2, "bf16"), (4096, 2, "f32")])
 def test_stage2_alone_on_random_partials(S, Hq, dtype):
     """The merge on seeded partials of every kind the split rule can leave:
     split log-sum-exps spread over +-20 (up to 80 apart within one row),
     empty splits (-inf) scattered and in runs, half of one request's rows
-    with every split empty.  Split counts on both sides of a lane's
-    register pass (16 splits per lane, so 16 and 256 at 1 and 16 lanes);
-    2 to 128 query heads (two requests) take the merge through 1 to 64
-    lanes per output."""
+    with every split empty.  Split counts on both sides of the lane rule's
+    steps (8 splits per lane up to 16 splits, then 16: 8 and 9, 16 and 17) and past
+    one register pass of 16 splits per lane at the 64-lane limit (2,000 and
+    4,096: two and four passes); 2 to 128 query heads (two requests) take
+    the merge through 1 to 64 lanes per output."""
     B, Hkv, D, P = 2, 2, 128, 16
     rng = np.random.default_rng(1000 + S)
     po = rng.standard_normal((B, 1, Hq, S, D))
