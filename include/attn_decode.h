@@ -301,6 +301,10 @@ typedef struct attn_decode_prefix_plan_t {
  * run cannot check: within a group the page-table rows hold the same page
  * ids in their first prefix_len / page_size entries, and every request has
  * ctx[b] >= prefix_len + q_len - 1 (each of its rows sees the whole prefix).
+ * The shared pass reads member gG's first prefix_len / page_size page ids
+ * whatever the members' ctx[b]: those entries must be valid page ids, or the
+ * kernels read out of bounds; a request shorter than the prefix gets wrong
+ * results, not an error.
  */
 attn_status attn_decode_plan_prefix(const attn_decode_desc* desc, int32_t max_context_len,
                                     int32_t prefix_group, int32_t prefix_len, int32_t flags,
