@@ -435,7 +435,9 @@ def measure_prefix(w, args, stream):
         "unique_kv_frac": round(touched / (us_op * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "tflops_per_s": round(algorithmic_flops(w) / (us_op * 1e-6) / 1e12, 2),
         "prefix_group": G, "prefix_len": w.prefix_len,
-        "shared_splits": plan.shared.num_splits if w.prefix_len else 0, "own_splits": plan.own.num_splits,
+        # below the planner's row threshold the plan is the default one (no shared pass)
+        "shared_pass": plan.prefix_len > 0,
+        "shared_splits": plan.shared.num_splits if plan.prefix_len else 0, "own_splits": plan.own.num_splits,
         "shared_rows_per_wg": plan.shared.rows_per_wg, "shared_head_tiles": plan.shared.head_tiles,
         "own_rows_per_wg": plan.own.rows_per_wg, "replicas": R, "kv_bytes_per_op": kv_bytes,
         "plan_key": str(plan.key),

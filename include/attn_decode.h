@@ -99,13 +99,16 @@ enum {
                                        MI355X merging a whole group's partials on one CU
                                        (with the per-XCD L2 write-back of each release)
                                        takes longer than the launch it saves */
-  ATTN_PLAN_PRIVATE_PAGES = 8       /* performance hint: no KV page is shared between the
+  ATTN_PLAN_PRIVATE_PAGES = 8,      /* performance hint: no KV page is shared between the
                                        batch's requests.  With 16-63 query rows per KV head
                                        the planner then takes the one-wave ring shape, which
                                        streams private pages faster, instead of four key
                                        streams, which compute four blocks at once and pay off
                                        when requests re-read shared prefix pages from the L2.
                                        Results do not depend on it (either shape is exact) */
+  ATTN_PLAN_SHARED_PASS = 16        /* shared-prefix plans only: run the shared pass even when
+                                       a group has fewer query rows than the planner's
+                                       threshold (attn_decode_plan_prefix) */
 };
 
 /* Kernel families the planner picks from. */
@@ -281,11 +284,13 @@ attn_status attn_decode_split_range(const attn_decode_plan_t* plan, int32_t cont
  * bytes; workspace_bytes is its size (rounded up to 256).  shared is unused
  * (all zero) when prefix_len is 0.
  */
+#define ATTN_SHARED_PASS_MIN_ROWS 128
+
 typedef struct attn_decode_prefix_plan_t {
   attn_decode_plan_t shared;  /* the groups' shared keys (virtual batch B / G, q_len G * q_len) */
   attn_decode_plan_t own;     /* every request's keys past the prefix */
   int32_t prefix_group;       /* G */
-  int32_t prefix_len;         /* shared keys per group */
+  int32_t prefix_len;         /* shared keys per group (0: no shared pass) */
   int32_t num_splits;         /* split slots per row */
   int32_t reserved;
   int64_t workspace_bytes;
@@ -295,9 +300,19 @@ typedef struct attn_decode_prefix_plan_t {
 /*
  * Plan a shared-prefix decode.  prefix_group G >= 1 must divide batch;
  * prefix_len must be a multiple of page_size with prefix_len + q_len - 1 <=
- * max_context_len; flags may hold ATTN_PLAN_NO_XCD_REMAP (the own pass is
- * always planned with ATTN_PLAN_PRIVATE_PAGES: its keys are private).
- * ATTN_EINVAL / ATTN_EUNSUPPORTED as attn_decode_plan.  Preconditions the
+ * max_context_len; flags may hold ATTN_PLAN_NO_XCD_REMAP,
+ * ATTN_PLAN_PRIVATE_PAGES and ATTN_PLAN_SHARED_PASS (the own pass is always
+ * planned with ATTN_PLAN_PRIVATE_PAGES: its keys are private).
+ * ATTN_EINVAL / ATTN_EUNSUPPORTED as attn_decode_plan.
+ * The shared pass runs when a group holds at least
+ * ATTN_SHARED_PASS_MIN_ROWS query rows per KV head (G * q_len * H_q / H_kv),
+ * or when ATTN_PLAN_SHARED_PASS is set.  With fewer rows the plan falls back
+ * to the default plan over all keys: prefix_len and shared are zero, own is
+ * what attn_decode_plan(desc, max_context_len, 0, flags) gives (the
+ * XCD-contiguous order then lets a group's requests share the prefix
+ * through one XCD's L2), and attn_decode_run_prefix runs it with the same
+ * bits as attn_decode_run.  On MI355X with 16 MLA heads the shared pass lost
+ * with groups of 1, 2 and 4 requests (16-64 rows) and won from 8 (128).  Preconditions the
  * run cannot check: within a group the page-table rows hold the same page
  * ids in their first prefix_len / page_size entries, and every request has
  * ctx[b] >= prefix_len + q_len - 1 (each of its rows sees the whole prefix).

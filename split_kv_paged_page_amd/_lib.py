@@ -23,6 +23,7 @@ ATTN_PLAN_POLICY_P2 = 1
 ATTN_PLAN_NO_XCD_REMAP = 2
 ATTN_PLAN_FUSED_MERGE = 4
 ATTN_PLAN_PRIVATE_PAGES = 8
+ATTN_PLAN_SHARED_PASS = 16
 ATTN_VARIANT_VALU, ATTN_VARIANT_MFMA = 1, 2
 
 EXPORTED = ["attn_decode_plan", "attn_decode_plan_lens", "attn_decode_run", "attn_decode_partials", "attn_decode_merge",
@@ -30,6 +31,7 @@ EXPORTED = ["attn_decode_plan", "attn_decode_plan_lens", "attn_decode_run", "att
             "attn_decode_run_noalloc", "attn_decode_plan_prefix", "attn_decode_run_prefix", "attn_decode_last_error"]
 NOALLOC_SCRATCH_BYTES = 64 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
 MAX_SPLIT_TABLE = 64               # ATTN_MAX_SPLIT_TABLE
+SHARED_PASS_MIN_ROWS = 128         # ATTN_SHARED_PASS_MIN_ROWS
 
 _STATUS = {ATTN_OK: "ATTN_OK", ATTN_EINVAL: "ATTN_EINVAL", ATTN_EUNSUPPORTED: "ATTN_EUNSUPPORTED",
            ATTN_EWORKSPACE: "ATTN_EWORKSPACE", ATTN_EHIP: "ATTN_EHIP"}
@@ -181,7 +183,9 @@ def attn_decode_plan_lens(desc: AttnDecodeDesc, host_context_lens, num_splits: i
 def attn_decode_plan_prefix(desc: AttnDecodeDesc, max_context_len: int, prefix_group: int, prefix_len: int,
                             flags: int = 0) -> AttnDecodePrefixPlan:
     """Plan for batches whose groups of prefix_group consecutive requests share
-    their first prefix_len keys (the same page ids)."""
+    their first prefix_len keys (the same page ids).  Groups with fewer than
+    SHARED_PASS_MIN_ROWS query rows per KV head get the default plan
+    (prefix_len 0 in the result) unless flags hold ATTN_PLAN_SHARED_PASS."""
     p = AttnDecodePrefixPlan()
     _check(lib().attn_decode_plan_prefix(ctypes.byref(desc), max_context_len, prefix_group, prefix_len, flags,
                                          ctypes.byref(p)))

@@ -607,10 +607,30 @@ attn_status attn_decode_plan_prefix(const attn_decode_desc* desc, int32_t max_co
   if ((int64_t)prefix_len + d.q_len - 1 > max_context_len)
     return fail(ATTN_EINVAL, "prefix_len + q_len - 1 (%lld) exceeds max_context_len %d",
                 (long long)prefix_len + d.q_len - 1, max_context_len);
-  if (flags & ~(ATTN_PLAN_NO_XCD_REMAP | ATTN_PLAN_PRIVATE_PAGES))
+  if (flags & ~(ATTN_PLAN_NO_XCD_REMAP | ATTN_PLAN_PRIVATE_PAGES | ATTN_PLAN_SHARED_PASS))
     return fail(ATTN_EINVAL, "unknown or unsupported plan flags 0x%x for a shared-prefix plan", flags);
   attn_decode_prefix_plan_t pp{};
   pp.prefix_group = prefix_group;
+  // Below ATTN_SHARED_PASS_MIN_ROWS rows per group the default plan is
+  // taken: its XCD-contiguous order already puts a split of a group's
+  // requests on one XCD, whose L2 serves them the prefix, and a shared pass
+  // over few rows needs many splits of its few virtual requests to fill the
+  // CUs, whose partials then weigh as much as the keys.  MLA, 16 heads, 68,000
+  // keys with 63,240 shared (us per op, shared-prefix plan / default plan):
+  // groups of 1, 2, 4 requests 36.5 / 25.2, 43.1 / 36.3, 60.3 / 48.7; of 8,
+  // at batch 8, 16, 48, 61.1 / 73.3, 81.1 / 114.4, 198.6 / 294.0.
+  const int64_t group_rows = (int64_t)prefix_group * d.q_len * (d.num_q_heads / d.num_kv_heads);
+  if (prefix_len > 0 && group_rows < ATTN_SHARED_PASS_MIN_ROWS && !(flags & ATTN_PLAN_SHARED_PASS)) {
+    st = plan_impl(&d, max_context_len, nullptr, 0, flags & ~ATTN_PLAN_SHARED_PASS, &pp.own);
+    if (st != ATTN_OK) return st;
+    pp.num_splits = pp.own.num_splits;
+    pp.workspace_bytes = pp.own.workspace_bytes;
+    const uint64_t parts[] = {pp.own.key, (uint64_t)prefix_group, 0};
+    pp.key = fnv1a(parts, sizeof(parts));
+    *plan = pp;
+    g_err[0] = 0;
+    return ATTN_OK;
+  }
   pp.prefix_len = prefix_len;
   if (prefix_len > 0) {
     // The groups' shared keys: group g is one request whose q_len * G rows

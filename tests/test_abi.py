@@ -349,6 +349,42 @@ def test_prefix_plan_passes_and_split_rule():
     assert p0.shared.num_splits == 0 and p0.num_splits == p0.own.num_splits
 
 
+def test_prefix_plan_falls_back_below_the_row_threshold():
+    """Groups with fewer than SHARED_PASS_MIN_ROWS query rows per KV head get
+    the default plan over every key (no shared pass) unless the caller
+    forces the shared pass; the caller's other flags reach that plan."""
+    assert sk.SHARED_PASS_MIN_ROWS == 128
+    d = mla_desc(48)
+    for G in (1, 2, 4):      # 16, 32, 64 rows
+        pp = sk.attn_decode_plan_prefix(d, 68000, G, 63240)
+        plain = sk.attn_decode_plan(d, 68000, 0, 0)
+        assert pp.prefix_len == 0 and pp.shared.num_splits == 0 and pp.prefix_group == G
+        assert pp.own.key == plain.key and pp.num_splits == plain.num_splits
+        assert pp.workspace_bytes == plain.workspace_bytes
+        forced = sk.attn_decode_plan_prefix(d, 68000, G, 63240, sk.ATTN_PLAN_SHARED_PASS)
+        assert forced.prefix_len == 63240 and forced.shared.num_splits > 0
+        assert forced.key != pp.key
+        assert not (forced.own.flags & sk.ATTN_PLAN_SHARED_PASS)
+    # the caller's flags reach the fallback plan
+    nr = sk.attn_decode_plan_prefix(d, 68000, 4, 63240, sk.ATTN_PLAN_NO_XCD_REMAP)
+    assert nr.own.flags == sk.ATTN_PLAN_NO_XCD_REMAP and nr.own.xcd_remap == 0
+    pv = sk.attn_decode_plan_prefix(d, 68000, 4, 63240, sk.ATTN_PLAN_PRIVATE_PAGES)
+    assert pv.own.key == sk.attn_decode_plan(d, 68000, 0, sk.ATTN_PLAN_PRIVATE_PAGES).key
+    # 8 MLA requests of 16 heads: 128 rows, the shared pass
+    assert sk.attn_decode_plan_prefix(d, 68000, 8, 63240).prefix_len == 63240
+    # GQA with 8 query heads per KV head: 16 requests (128 rows) share, 8 do not;
+    # draft rows count too (4 positions x 8 heads x 4 requests)
+    g = desc(B=16)
+    assert sk.attn_decode_plan_prefix(g, 65536, 16, 1024).prefix_len == 1024
+    assert sk.attn_decode_plan_prefix(g, 65536, 8, 1024).prefix_len == 0
+    dr = desc(B=8, q_len=4, Hq=32, Hkv=4, Dk=256, Dv=256, causal=1)
+    assert sk.attn_decode_plan_prefix(dr, 2048, 4, 1024).prefix_len == 1024
+    assert sk.attn_decode_plan_prefix(dr, 2048, 2, 1024).prefix_len == 0
+    # validation comes first: a prefix too long for the context fails either way
+    with pytest.raises(sk.AttnDecodeError):
+        sk.attn_decode_plan_prefix(dr, 2048, 2, 2048)
+
+
 @pytest.mark.parametrize("args,status", [
     ((7, 100), sk.ATTN_EINVAL),        # group does not divide the batch
     ((0, 100), sk.ATTN_EINVAL),
@@ -364,7 +400,7 @@ def test_prefix_plan_rejects(args, status):
 
 def test_prefix_plan_flags_and_run_errors():
     d = desc(B=16, Hq=16, Hkv=1, Dk=576, Dv=512, P=1, maxp=68000, alias=1, pages=655360)
-    for bad in (sk.ATTN_PLAN_FUSED_MERGE, sk.ATTN_PLAN_POLICY_P2, 16):
+    for bad in (sk.ATTN_PLAN_FUSED_MERGE, sk.ATTN_PLAN_POLICY_P2, 32):
         with pytest.raises(sk.AttnDecodeError) as ei:
             sk.attn_decode_plan_prefix(d, 1000, 8, 600, bad)
         assert ei.value.status == sk.ATTN_EINVAL

@@ -18,9 +18,11 @@ pytestmark = pytest.mark.gpu
 
 
 class PrefixDecode:
-    """One uploaded problem + shared-prefix plan."""
+    """One uploaded problem + shared-prefix plan.  The small cases have
+    fewer rows per group than the planner's threshold for a shared pass, so
+    the mechanism tests force it (ATTN_PLAN_SHARED_PASS)."""
 
-    def __init__(self, inp, flags=0):
+    def __init__(self, inp, flags=sk.ATTN_PLAN_SHARED_PASS):
         import torch
         validate_inputs(inp)
         w = inp.w
@@ -32,7 +34,8 @@ class PrefixDecode:
         mx = int(max(inp.context_lens))
         self.plan = sk.attn_decode_plan_prefix(self.desc, mx, w.prefix_group, w.prefix_len, flags)
         self.S = self.plan.num_splits
-        self.Sp = self.plan.shared.num_splits if w.prefix_len else 0
+        self.prefix = self.plan.prefix_len
+        self.Sp = self.plan.shared.num_splits if self.prefix else 0
         self.So = self.plan.own.num_splits
         assert self.S == self.Sp + self.So
         self.dtype = torch.float32 if w.kv_dtype == "f32" else torch.bfloat16
@@ -53,8 +56,7 @@ class PrefixDecode:
         return self
 
     def bounds_of(self):
-        w = self.inp.w
-        return lambda L: oracle.prefix_split_bounds(L, w.prefix_len, self.Sp, self.So)
+        return lambda L: oracle.prefix_split_bounds(L, self.prefix, self.Sp, self.So)
 
     def split_parts(self):
         w = self.inp.w
@@ -205,6 +207,39 @@ def test_prefix_full_size_mla_b48_sampled():
     d = PrefixDecode(inp).run()
     say(f"prefix mla_b48 S = {d.Sp} + {d.So}")
     check(d, requests=(0, 9, 47))
+
+
+@pytest.mark.parametrize("name", ["gqa_b4_g2", "drafts_g3", "mla_wide_b4_g2"])
+def test_prefix_fallback_is_the_plain_run(name):
+    """Groups below the planner's row threshold (16, 96 and 256 rows per
+    group here; the last is above it) without ATTN_PLAN_SHARED_PASS: below,
+    the plan is the default plan over every key and attn_decode_run_prefix
+    gives attn_decode_run's bits; above, the shared pass runs."""
+    import torch
+    inp = inputs(name)
+    w = inp.w
+    d = PrefixDecode(inp, flags=0).run()
+    rows = w.prefix_group * w.q_len * (w.num_q_heads // w.num_kv_heads)
+    say(f"prefix fallback {name}: {rows} rows per group, S = {d.Sp} + {d.So}")
+    if rows >= sk.SHARED_PASS_MIN_ROWS:
+        assert d.prefix == w.prefix_len and d.Sp > 0
+        check(d)
+        return
+    assert d.prefix == 0 and d.Sp == 0
+    check(d)
+    t = d.t
+    v = t["k_cache"] if t["v_cache"] is None else t["v_cache"]
+    plan = sk.attn_decode_plan(d.desc, int(max(inp.context_lens)))
+    assert plan.key == d.plan.own.key and plan.num_splits == d.S
+    ws = torch.empty(plan.workspace_bytes // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(d.out)
+    lse = torch.empty_like(d.lse)
+    sk.attn_decode_run(plan, t["q"], t["k_cache"], v, t["page_table"], t["context_lens"], float(inp.scale), 0,
+                       out, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(d.out.view(torch.int16) if d.out.dtype == torch.bfloat16 else d.out.view(torch.int32),
+                       out.view(torch.int16) if out.dtype == torch.bfloat16 else out.view(torch.int32))
+    assert torch.equal(d.lse.view(torch.int32), lse.view(torch.int32))
 
 
 @pytest.mark.parametrize("name", ["mla_b16_p700", "gqa_b4_g2"])
