@@ -76,7 +76,9 @@ struct MCfg {
   // 13.6 / 14.4, prefill 4 x 2048 at head dim 128 139 / 162 (the smaller
   // ring also lets a third workgroup onto the CU), wide MLA 379 / 380.
   // Again for the lone wave at head dim 128 with one workgroup per CU:
-  // 2 / 3 / 4 / 5 tiles, stage 1 18.6 / 15.4 / 15.9 / 16.3 us.
+  // 2 / 3 / 4 / 5 tiles, stage 1 18.6 / 15.4 / 15.9 / 16.3 us; and for the
+  // drafts' work list of 128-key splits, where 4 tiles put all four blocks
+  // of a workgroup in flight at once: 10.0 against 10.7 us.
   // The four-wave shape at head dim 128 (prefill, whose keys mostly come
   // from cache) takes 2 tiles, which fits a fourth workgroup per CU: whole
   // op 4 x 2048 132.3 -> 128.0 us, varlen 95.0 -> 90.8.
