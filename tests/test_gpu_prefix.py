@@ -95,6 +95,64 @@ def cases():
     }
 
 
+def random_prefix_cases(n=24, seed=20261204):
+    """Seeded random shared-prefix shapes: bf16 at head dims 64-256 and MLA
+    576/512, fp32 at 64 and 128; 1-16 query heads per KV head, q_len 1-5
+    with and without causal rows; groups of 1-4 requests, one or two groups;
+    page sizes 1-32; prefixes of 0 to about 1,200 keys (whole pages) and own
+    parts from none to 1,500 keys, every request holding the prefix plus
+    q_len - 1 keys at least."""
+    import dataclasses
+    rng = np.random.default_rng(seed)
+    base = get("gqa_64k")
+    out = {}
+    for i in range(n):
+        kind = rng.choice(["bf16", "bf16", "mla", "f32"])
+        if kind == "mla":
+            dk, dv, alias, dt, hkv = 576, 512, True, "bf16", 1
+            hq = int(rng.integers(1, 33))
+            P = int(rng.choice([1, 16]))
+        else:
+            dk = dv = int(rng.choice([64, 128] if kind == "f32" else [64, 128, 256]))
+            alias, dt = False, ("f32" if kind == "f32" else "bf16")
+            hkv = int(rng.integers(1, 4))
+            hq = hkv * int(rng.integers(1, 17))
+            P = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        q_len = int(rng.choice([1] * 5 + [2, 4, 5]))
+        while (hq // hkv) * q_len > 128:
+            q_len = max(1, q_len // 2)
+        causal = bool(q_len > 1 and rng.random() < 0.7)
+        G = int(rng.integers(1, 5))
+        B = G * int(rng.integers(1, 3))
+        prefix = P * int(rng.integers(0, 1200 // P + 1))
+        own = rng.integers(0, 1500, B)
+        own[rng.random(B) < 0.2] = 0
+        ctx = tuple(int(prefix + q_len - 1 + o) for o in own)
+        w = dataclasses.replace(base, name=f"prand{i}", batch=B, q_len=q_len, num_q_heads=hq, num_kv_heads=hkv,
+                                head_dim_qk=dk, head_dim_v=dv, page_size=P, kv_dtype=dt, context_lens=ctx,
+                                v_aliases_k=alias, causal=causal, num_splits=0, seed=2000 + i,
+                                prefix_group=G, prefix_len=prefix)
+        out[f"prand{i:02d}"] = dataclasses.replace(w, pool_pages=2 * w.pages_needed() + 3)
+    return out
+
+
+_RANDOM = random_prefix_cases()
+
+
+@pytest.mark.parametrize("name", list(_RANDOM))
+def test_prefix_parity_random_shapes(name):
+    """Every output, log-sum-exp and split slot against the oracle, with the
+    shared pass forced (and, where the group is big enough, also chosen)."""
+    w = _RANDOM[name]
+    say(f"prefix random {name}: {w.kv_dtype} B={w.batch} G={w.prefix_group} prefix={w.prefix_len} "
+        f"q_len={w.q_len} heads={w.num_q_heads}/{w.num_kv_heads} dims={w.head_dim_qk}/{w.head_dim_v} "
+        f"P={w.page_size} causal={w.causal} ctx={w.context_lens}")
+    d = PrefixDecode(generate(w))
+    say(f"  S = {d.Sp} + {d.So}")
+    e = check(d.run())
+    say(f"  out {e[0]:.2e} lse {e[1]:.2e}")
+
+
 _INPUTS = {}
 
 
