@@ -106,9 +106,9 @@ enum {
                                        streams, which compute four blocks at once and pay off
                                        when requests re-read shared prefix pages from the L2.
                                        Results do not depend on it (either shape is exact) */
-  ATTN_PLAN_SHARED_PASS = 16        /* shared-prefix plans only: run the shared pass even when
-                                       a group has fewer query rows than the planner's
-                                       threshold (attn_decode_plan_prefix) */
+  ATTN_PLAN_SHARED_PASS = 16        /* shared-prefix plans only: run the shared pass where the
+                                       planner would take the default plan
+                                       (attn_decode_plan_prefix) */
 };
 
 /* Kernel families the planner picks from. */
@@ -304,15 +304,19 @@ typedef struct attn_decode_prefix_plan_t {
  * ATTN_PLAN_PRIVATE_PAGES and ATTN_PLAN_SHARED_PASS (the own pass is always
  * planned with ATTN_PLAN_PRIVATE_PAGES: its keys are private).
  * ATTN_EINVAL / ATTN_EUNSUPPORTED as attn_decode_plan.
- * The shared pass runs when a group holds at least
- * ATTN_SHARED_PASS_MIN_ROWS query rows per KV head (G * q_len * H_q / H_kv),
- * or when ATTN_PLAN_SHARED_PASS is set.  With fewer rows the plan falls back
- * to the default plan over all keys: prefix_len and shared are zero, own is
- * what attn_decode_plan(desc, max_context_len, 0, flags) gives (the
- * XCD-contiguous order then lets a group's requests share the prefix
- * through one XCD's L2), and attn_decode_run_prefix runs it with the same
- * bits as attn_decode_run.  On MI355X with 16 MLA heads the shared pass lost
- * with groups of 1, 2 and 4 requests (16-64 rows) and won from 8 (128).  Preconditions the
+ * Unless ATTN_PLAN_SHARED_PASS is set, the plan falls back to the default
+ * plan over all keys when the shared pass would not pay: for groups of one
+ * request (G = 1), and when the default plan takes the four-key-stream shape
+ * (matrix cores, 16-63 query rows per KV head in a batch that may share
+ * pages, whose XCD-contiguous order lets a group's requests share the
+ * prefix through one XCD's L2) and a group holds fewer than
+ * ATTN_SHARED_PASS_MIN_ROWS query rows per KV head (G * q_len * H_q / H_kv).
+ * The fallback plan has prefix_len and shared zero and own equal to
+ * attn_decode_plan(desc, max_context_len, 0, flags); attn_decode_run_prefix
+ * runs it with the same bits as attn_decode_run.  On MI355X the shared pass
+ * lost for MLA with 16 heads in groups of 1, 2 and 4 requests and won from 8;
+ * for GQA with 8 query heads per KV head (the one-wave shape) it won by
+ * 1.4-3.2x from groups of 4.  Preconditions the
  * run cannot check: within a group the page-table rows hold the same page
  * ids in their first prefix_len / page_size entries, and every request has
  * ctx[b] >= prefix_len + q_len - 1 (each of its rows sees the whole prefix).

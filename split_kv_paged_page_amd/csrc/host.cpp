@@ -611,25 +611,38 @@ attn_status attn_decode_plan_prefix(const attn_decode_desc* desc, int32_t max_co
     return fail(ATTN_EINVAL, "unknown or unsupported plan flags 0x%x for a shared-prefix plan", flags);
   attn_decode_prefix_plan_t pp{};
   pp.prefix_group = prefix_group;
-  // Below ATTN_SHARED_PASS_MIN_ROWS rows per group the default plan is
-  // taken: its XCD-contiguous order already puts a split of a group's
-  // requests on one XCD, whose L2 serves them the prefix, and a shared pass
-  // over few rows needs many splits of its few virtual requests to fill the
-  // CUs, whose partials then weigh as much as the keys.  MLA, 16 heads, 68,000
-  // keys with 63,240 shared (us per op, shared-prefix plan / default plan):
-  // groups of 1, 2, 4 requests 36.5 / 25.2, 43.1 / 36.3, 60.3 / 48.7; of 8,
-  // at batch 8, 16, 48, 61.1 / 73.3, 81.1 / 114.4, 198.6 / 294.0.
-  const int64_t group_rows = (int64_t)prefix_group * d.q_len * (d.num_q_heads / d.num_kv_heads);
-  if (prefix_len > 0 && group_rows < ATTN_SHARED_PASS_MIN_ROWS && !(flags & ATTN_PLAN_SHARED_PASS)) {
-    st = plan_impl(&d, max_context_len, nullptr, 0, flags & ~ATTN_PLAN_SHARED_PASS, &pp.own);
+  // When the shared pass does not pay, the default plan is taken: with
+  // groups of one request nothing is shared, and where the default plan
+  // runs four key streams per 16-row tile (16-63 rows per KV head, a batch
+  // that may share pages) its XCD-contiguous order already serves a split's
+  // prefix blocks to the group's requests from one XCD's L2.  There a shared
+  // pass over fewer than ATTN_SHARED_PASS_MIN_ROWS rows needs many splits of
+  // its few virtual requests to fill the CUs, and their partials weigh as
+  // much as the keys.  Measured (us per op, shared-prefix plan / default
+  // plan, 61,440 or 63,240 of 65,536 or 68,000 keys shared):
+  //   MLA, 16 heads (key streams): groups of 1, 2, 4 requests 36.5 / 25.2,
+  //   43.1 / 36.3, 60.3 / 48.7; of 8 at batch 8, 16, 48 61.1 / 73.3,
+  //   81.1 / 114.4, 198.6 / 294.0;
+  //   GQA, 8 heads per KV head (one-wave ring, little L2 reuse): groups of 1
+  //   at batch 4 56.6 / 51.8; of 2 at batch 2 and 8 23.9 / 26.4 and
+  //   62.3 / 84.4; of 4 at batch 4 32.9 / 45.5; of 8 at batch 8 and 16
+  //   34.9 / 83.9 and 50.0 / 160.6; of 16 at batch 16 52.3 / 160.3.
+  if (prefix_len > 0 && !(flags & ATTN_PLAN_SHARED_PASS)) {
+    attn_decode_plan_t def{};
+    st = plan_impl(&d, max_context_len, nullptr, 0, flags, &def);
     if (st != ATTN_OK) return st;
-    pp.num_splits = pp.own.num_splits;
-    pp.workspace_bytes = pp.own.workspace_bytes;
-    const uint64_t parts[] = {pp.own.key, (uint64_t)prefix_group, 0};
-    pp.key = fnv1a(parts, sizeof(parts));
-    *plan = pp;
-    g_err[0] = 0;
-    return ATTN_OK;
+    const int64_t group_rows = (int64_t)prefix_group * d.q_len * (d.num_q_heads / d.num_kv_heads);
+    const bool key_streams = def.variant == ATTN_VARIANT_MFMA && def.stage1_waves * 16 > def.rows_per_wg;
+    if (prefix_group == 1 || (key_streams && group_rows < ATTN_SHARED_PASS_MIN_ROWS)) {
+      pp.own = def;
+      pp.num_splits = def.num_splits;
+      pp.workspace_bytes = def.workspace_bytes;
+      const uint64_t parts[] = {def.key, (uint64_t)prefix_group, 0};
+      pp.key = fnv1a(parts, sizeof(parts));
+      *plan = pp;
+      g_err[0] = 0;
+      return ATTN_OK;
+    }
   }
   pp.prefix_len = prefix_len;
   if (prefix_len > 0) {

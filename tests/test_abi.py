@@ -349,40 +349,66 @@ def test_prefix_plan_passes_and_split_rule():
     assert p0.shared.num_splits == 0 and p0.num_splits == p0.own.num_splits
 
 
-def test_prefix_plan_falls_back_below_the_row_threshold():
-    """Groups with fewer than SHARED_PASS_MIN_ROWS query rows per KV head get
-    the default plan over every key (no shared pass) unless the caller
-    forces the shared pass; the caller's other flags reach that plan."""
+def test_prefix_plan_falls_back_where_the_shared_pass_does_not_pay():
+    """Without ATTN_PLAN_SHARED_PASS the plan is the default plan over every
+    key for groups of one request, and where the default plan runs four key
+    streams (16-63 rows per KV head) with fewer than SHARED_PASS_MIN_ROWS
+    rows per group; the caller's other flags reach that plan."""
     assert sk.SHARED_PASS_MIN_ROWS == 128
-    d = mla_desc(48)
-    for G in (1, 2, 4):      # 16, 32, 64 rows
-        pp = sk.attn_decode_plan_prefix(d, 68000, G, 63240)
-        plain = sk.attn_decode_plan(d, 68000, 0, 0)
+
+    def check_fallback(d, mx, G, prefix, flags=0):
+        pp = sk.attn_decode_plan_prefix(d, mx, G, prefix, flags)
+        plain = sk.attn_decode_plan(d, mx, 0, flags)
         assert pp.prefix_len == 0 and pp.shared.num_splits == 0 and pp.prefix_group == G
         assert pp.own.key == plain.key and pp.num_splits == plain.num_splits
         assert pp.workspace_bytes == plain.workspace_bytes
-        forced = sk.attn_decode_plan_prefix(d, 68000, G, 63240, sk.ATTN_PLAN_SHARED_PASS)
-        assert forced.prefix_len == 63240 and forced.shared.num_splits > 0
-        assert forced.key != pp.key
+        forced = sk.attn_decode_plan_prefix(d, mx, G, prefix, flags | sk.ATTN_PLAN_SHARED_PASS)
+        assert forced.prefix_len == prefix and forced.shared.num_splits > 0 and forced.key != pp.key
         assert not (forced.own.flags & sk.ATTN_PLAN_SHARED_PASS)
+        return pp
+
+    def shared(d, mx, G, prefix):
+        pp = sk.attn_decode_plan_prefix(d, mx, G, prefix)
+        assert pp.prefix_len == prefix and pp.shared.num_splits > 0
+        return pp
+
+    # MLA, 16 heads: the default plan runs key streams; 16, 32, 64 rows fall
+    # back, 8 requests (128 rows) share
+    d = mla_desc(48)
+    assert sk.attn_decode_plan(d, 68000).stage1_waves == 4 and sk.attn_decode_plan(d, 68000).rows_per_wg == 16
+    for G in (1, 2, 4):
+        check_fallback(d, 68000, G, 63240)
+    shared(d, 68000, 8, 63240)
     # the caller's flags reach the fallback plan
-    nr = sk.attn_decode_plan_prefix(d, 68000, 4, 63240, sk.ATTN_PLAN_NO_XCD_REMAP)
+    nr = check_fallback(d, 68000, 4, 63240, sk.ATTN_PLAN_NO_XCD_REMAP)
     assert nr.own.flags == sk.ATTN_PLAN_NO_XCD_REMAP and nr.own.xcd_remap == 0
+    # with the private-pages hint the default plan is the one-wave ring: shared
     pv = sk.attn_decode_plan_prefix(d, 68000, 4, 63240, sk.ATTN_PLAN_PRIVATE_PAGES)
-    assert pv.own.key == sk.attn_decode_plan(d, 68000, 0, sk.ATTN_PLAN_PRIVATE_PAGES).key
-    # 8 MLA requests of 16 heads: 128 rows, the shared pass
-    assert sk.attn_decode_plan_prefix(d, 68000, 8, 63240).prefix_len == 63240
-    # GQA with 8 query heads per KV head: 16 requests (128 rows) share, 8 do not;
-    # draft rows count too (4 positions x 8 heads x 4 requests)
+    assert pv.prefix_len == 63240
+    # GQA, 8 heads per KV head: the default plan is the one-wave ring, so
+    # every group of two or more shares; a group of one never does
     g = desc(B=16)
-    assert sk.attn_decode_plan_prefix(g, 65536, 16, 1024).prefix_len == 1024
-    assert sk.attn_decode_plan_prefix(g, 65536, 8, 1024).prefix_len == 0
+    assert sk.attn_decode_plan(g, 65536).stage1_waves == 1
+    for G in (2, 4, 8, 16):
+        shared(g, 65536, G, 1024)
+    check_fallback(g, 65536, 1, 1024)
+    # GQA with 16 heads per KV head (key streams at 16-63 rows): 2 requests
+    # (32 rows) fall back, 8 (128 rows) share
+    g16 = desc(B=16, Hq=32, Hkv=2)
+    check_fallback(g16, 65536, 2, 1024)
+    shared(g16, 65536, 8, 1024)
+    # draft rows (4 positions x 8 heads = 32 rows at head dim 256: two row
+    # tiles on a ring): groups of two share
     dr = desc(B=8, q_len=4, Hq=32, Hkv=4, Dk=256, Dv=256, causal=1)
-    assert sk.attn_decode_plan_prefix(dr, 2048, 4, 1024).prefix_len == 1024
-    assert sk.attn_decode_plan_prefix(dr, 2048, 2, 1024).prefix_len == 0
+    shared(dr, 2048, 2, 1024)
+    check_fallback(dr, 2048, 1, 1024)
+    # fp32 (vector ALUs): only groups of one fall back
+    f = desc(B=8, Hq=4, Hkv=1, Dk=64, Dv=64, dtype=sk.ATTN_F32)
+    shared(f, 4096, 2, 1024)
+    check_fallback(f, 4096, 1, 1024)
     # validation comes first: a prefix too long for the context fails either way
     with pytest.raises(sk.AttnDecodeError):
-        sk.attn_decode_plan_prefix(dr, 2048, 2, 2048)
+        sk.attn_decode_plan_prefix(dr, 2048, 1, 2048)
 
 
 @pytest.mark.parametrize("args,status", [

@@ -18,9 +18,9 @@ pytestmark = pytest.mark.gpu
 
 
 class PrefixDecode:
-    """One uploaded problem + shared-prefix plan.  The small cases have
-    fewer rows per group than the planner's threshold for a shared pass, so
-    the mechanism tests force it (ATTN_PLAN_SHARED_PASS)."""
+    """One uploaded problem + shared-prefix plan.  The mechanism tests force
+    the shared pass (ATTN_PLAN_SHARED_PASS), which the planner skips for some
+    of the small cases."""
 
     def __init__(self, inp, flags=sk.ATTN_PLAN_SHARED_PASS):
         import torch
@@ -92,6 +92,12 @@ def cases():
         # prefix 0: the own pass alone over every key
         "gqa_b4_p0": scaled("gqa_64k", context_lens=(3000, 1500, 1025, 5000), prefix_group=2, prefix_len=0,
                             seed=67),
+        # MLA in groups of 2 (32 rows): the planner keeps the default plan
+        "mla_b4_g2": scaled("mla_b48", context_lens=(1000, 900, 1200, 701), prefix_group=2, prefix_len=700,
+                            seed=69),
+        # groups of one request: nothing to share
+        "gqa_b3_g1": scaled("gqa_64k", context_lens=(2000, 1100, 3000), prefix_group=1, prefix_len=1024,
+                            seed=70),
     }
 
 
@@ -267,24 +273,22 @@ def test_prefix_full_size_mla_b48_sampled():
     check(d, requests=(0, 9, 47))
 
 
-@pytest.mark.parametrize("name", ["gqa_b4_g2", "drafts_g3", "mla_wide_b4_g2"])
-def test_prefix_fallback_is_the_plain_run(name):
-    """Groups below the planner's row threshold (16, 96 and 256 rows per
-    group here; the last is above it) without ATTN_PLAN_SHARED_PASS: below,
-    the plan is the default plan over every key and attn_decode_run_prefix
-    gives attn_decode_run's bits; above, the shared pass runs."""
+@pytest.mark.parametrize("name,falls_back", [("mla_b4_g2", True), ("gqa_b3_g1", True), ("gqa_b4_g2", False),
+                                              ("drafts_g3", False), ("mla_b16_p700", False)])
+def test_prefix_fallback_is_the_plain_run(name, falls_back):
+    """Without ATTN_PLAN_SHARED_PASS: where the planner keeps the default plan
+    (MLA in groups of 2, groups of one request) attn_decode_run_prefix gives
+    attn_decode_run's bits; elsewhere the shared pass runs and matches the
+    oracle."""
     import torch
     inp = inputs(name)
-    w = inp.w
     d = PrefixDecode(inp, flags=0).run()
-    rows = w.prefix_group * w.q_len * (w.num_q_heads // w.num_kv_heads)
-    say(f"prefix fallback {name}: {rows} rows per group, S = {d.Sp} + {d.So}")
-    if rows >= sk.SHARED_PASS_MIN_ROWS:
-        assert d.prefix == w.prefix_len and d.Sp > 0
-        check(d)
+    say(f"prefix fallback {name}: S = {d.Sp} + {d.So}")
+    check(d)
+    if not falls_back:
+        assert d.prefix == inp.w.prefix_len and d.Sp > 0
         return
     assert d.prefix == 0 and d.Sp == 0
-    check(d)
     t = d.t
     v = t["k_cache"] if t["v_cache"] is None else t["v_cache"]
     plan = sk.attn_decode_plan(d.desc, int(max(inp.context_lens)))
@@ -295,8 +299,7 @@ def test_prefix_fallback_is_the_plain_run(name):
     sk.attn_decode_run(plan, t["q"], t["k_cache"], v, t["page_table"], t["context_lens"], float(inp.scale), 0,
                        out, lse, ws)
     torch.cuda.synchronize()
-    assert torch.equal(d.out.view(torch.int16) if d.out.dtype == torch.bfloat16 else d.out.view(torch.int32),
-                       out.view(torch.int16) if out.dtype == torch.bfloat16 else out.view(torch.int32))
+    assert torch.equal(d.out.view(torch.int16), out.view(torch.int16))
     assert torch.equal(d.lse.view(torch.int32), lse.view(torch.int32))
 
 
