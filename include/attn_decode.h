@@ -104,7 +104,10 @@ enum {
                                        the planner then takes the one-wave ring shape, which
                                        streams private pages faster, instead of four key
                                        streams, which compute four blocks at once and pay off
-                                       when requests re-read shared prefix pages from the L2.
+                                       when requests re-read shared prefix pages from the L2;
+                                       and with fewer rows at head dim 128, one one-wave
+                                       workgroup per CU instead of two (two keep the CUs'
+                                       work rate up when the L2 serves shared pages).
                                        Results do not depend on it (either shape is exact) */
   ATTN_PLAN_SHARED_PASS = 16        /* shared-prefix plans only: run the shared pass where the
                                        planner would take the default plan
@@ -305,18 +308,20 @@ typedef struct attn_decode_prefix_plan_t {
  * planned with ATTN_PLAN_PRIVATE_PAGES: its keys are private).
  * ATTN_EINVAL / ATTN_EUNSUPPORTED as attn_decode_plan.
  * Unless ATTN_PLAN_SHARED_PASS is set, the plan falls back to the default
- * plan over all keys when the shared pass would not pay: for groups of one
- * request (G = 1), and when the default plan takes the four-key-stream shape
- * (matrix cores, 16-63 query rows per KV head in a batch that may share
- * pages, whose XCD-contiguous order lets a group's requests share the
- * prefix through one XCD's L2) and a group holds fewer than
- * ATTN_SHARED_PASS_MIN_ROWS query rows per KV head (G * q_len * H_q / H_kv).
- * The fallback plan has prefix_len and shared zero and own equal to
- * attn_decode_plan(desc, max_context_len, 0, flags); attn_decode_run_prefix
- * runs it with the same bits as attn_decode_run.  On MI355X the shared pass
- * lost for MLA with 16 heads in groups of 1, 2 and 4 requests and won from 8;
- * for GQA with 8 query heads per KV head (the one-wave shape) it won by
- * 1.4-3.2x from groups of 4.  Preconditions the
+ * plan over all keys where the shared pass did not pay on MI355X.  With R =
+ * G * q_len * H_q / H_kv query rows per group and KV head, that is: G = 1;
+ * R < 32; a single group (G = batch) with R < 64; and a default plan on the
+ * four-key-stream shape (matrix cores, 16-63 query rows per KV head in a
+ * batch that may share pages) with R < ATTN_SHARED_PASS_MIN_ROWS.  The
+ * default plan's XCD-contiguous order then lets a group's requests share
+ * the prefix through one XCD's L2.  The fallback plan has prefix_len and
+ * shared zero and own equal to attn_decode_plan(desc, max_context_len, 0,
+ * flags); attn_decode_run_prefix runs it with the same bits as
+ * attn_decode_run.  Measured: MLA with 16 heads, the shared pass lost in
+ * groups of 1, 2 and 4 requests and won from 8 (294 -> 199 us at batch
+ * 48); GQA with 8 query heads per KV head lost in groups of 2, and in one
+ * group of 4, and won in four groups of 4 and from groups of 8 (89.6 ->
+ * 49.6 us at batch 16 in groups of 8).  Preconditions the
  * run cannot check: within a group the page-table rows hold the same page
  * ids in their first prefix_len / page_size entries, and every request has
  * ctx[b] >= prefix_len + q_len - 1 (each of its rows sees the whole prefix).

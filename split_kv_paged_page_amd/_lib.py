@@ -184,10 +184,8 @@ def attn_decode_plan_prefix(desc: AttnDecodeDesc, max_context_len: int, prefix_g
                             flags: int = 0) -> AttnDecodePrefixPlan:
     """Plan for batches whose groups of prefix_group consecutive requests share
     their first prefix_len keys (the same page ids).  Where the shared pass
-    would not pay (groups of one request; the key-stream shape with fewer
-    than SHARED_PASS_MIN_ROWS query rows per group and KV head) the result
-    is the default plan (prefix_len 0) unless flags hold
-    ATTN_PLAN_SHARED_PASS."""
+    would not pay (the rule in include/attn_decode.h) the result is the
+    default plan (prefix_len 0) unless flags hold ATTN_PLAN_SHARED_PASS."""
     p = AttnDecodePrefixPlan()
     _check(lib().attn_decode_plan_prefix(ctypes.byref(desc), max_context_len, prefix_group, prefix_len, flags,
                                          ctypes.byref(p)))

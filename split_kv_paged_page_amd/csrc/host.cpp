@@ -388,9 +388,17 @@ attn_status plan_impl(const attn_decode_desc* desc, int32_t max_context_len, con
     // and one such workgroup per CU walked twice the keys at the same rate
     // with half the partials to merge: 64K GQA whole op 18.73 -> 18.25 us,
     // and 52.3 -> 51.7 / 99.3 -> 98.0 at batch 4 / 8 (30.2 -> 30.4 at 2).
+    // That holds for one request and for private pages (the hint).  A
+    // batch whose requests may share pages keeps two per CU: once the L2
+    // serves the shared blocks, the wave's own per-block work bounds it.
+    // 64K GQA with 61,440 keys shared (one / two per CU, us per op): batch
+    // 4 in one group 45.8 / 29.5, 8 in one group 84.6 / 49.2, 16 in groups
+    // of 8 161.3 / 89.9; private batches of 4 and 8 unchanged (51.5 / 51.4,
+    // 98.2 / 98.2).
     // At head dim 64 (8 KB blocks) one per CU was far slower (stage 1 9.96
     // -> 12.0 us): two keep enough bytes in flight.
-    const bool one_wave_d128 = ms.rw == 1 && ms.kw == 1 && d.head_dim_qk == 128;
+    const bool one_wave_d128 =
+        ms.rw == 1 && ms.kw == 1 && d.head_dim_qk == 128 && (d.batch == 1 || (flags & ATTN_PLAN_PRIVATE_PAGES));
     wgs_per_cu = kLdsPerCu / ms.smem < 2 || one_wave_d128 ? 1 : 2;
   } else {
     const int rt = pick_rows_per_wg(d.dtype, d.head_dim_qk, d.head_dim_v, rows);
@@ -611,29 +619,37 @@ attn_status attn_decode_plan_prefix(const attn_decode_desc* desc, int32_t max_co
     return fail(ATTN_EINVAL, "unknown or unsupported plan flags 0x%x for a shared-prefix plan", flags);
   attn_decode_prefix_plan_t pp{};
   pp.prefix_group = prefix_group;
-  // When the shared pass does not pay, the default plan is taken: with
-  // groups of one request nothing is shared, and where the default plan
-  // runs four key streams per 16-row tile (16-63 rows per KV head, a batch
-  // that may share pages) its XCD-contiguous order already serves a split's
-  // prefix blocks to the group's requests from one XCD's L2.  There a shared
-  // pass over fewer than ATTN_SHARED_PASS_MIN_ROWS rows needs many splits of
-  // its few virtual requests to fill the CUs, and their partials weigh as
-  // much as the keys.  Measured (us per op, shared-prefix plan / default
-  // plan, 61,440 or 63,240 of 65,536 or 68,000 keys shared):
+  // When the shared pass does not pay, the default plan is taken:
+  //   * groups of one request: nothing is shared;
+  //   * fewer than 32 rows per group and KV head: a shared block then feeds
+  //     at most two 16-row tiles' worth of rows, which the default plan's
+  //     XCD-contiguous order also serves from one XCD's L2;
+  //   * one group, fewer than 64 rows: the shared pass is then a single
+  //     virtual request, cut into as many splits as fill the CUs (partials
+  //     that weigh as much as the keys) and run in the plain order;
+  //   * a default plan on four key streams per 16-row tile (16-63 rows per
+  //     KV head in a batch that may share pages), fewer than
+  //     ATTN_SHARED_PASS_MIN_ROWS rows: its streams already take a split's
+  //     prefix blocks from the L2 four at a time.
+  // Measured (us per op, shared-prefix plan / default plan; 61,440 of
+  // 65,536 or 63,240 of 68,000 keys shared):
   //   MLA, 16 heads (key streams): groups of 1, 2, 4 requests 36.5 / 25.2,
   //   43.1 / 36.3, 60.3 / 48.7; of 8 at batch 8, 16, 48 61.1 / 73.3,
   //   81.1 / 114.4, 198.6 / 294.0;
-  //   GQA, 8 heads per KV head (one-wave ring, little L2 reuse): groups of 1
-  //   at batch 4 56.6 / 51.8; of 2 at batch 2 and 8 23.9 / 26.4 and
-  //   62.3 / 84.4; of 4 at batch 4 32.9 / 45.5; of 8 at batch 8 and 16
-  //   34.9 / 83.9 and 50.0 / 160.6; of 16 at batch 16 52.3 / 160.3.
+  //   GQA, 8 query heads per KV head (one-wave ring, two workgroups per CU):
+  //   groups of 2 at batch 2, 8 and 16 24.0 / 20.3, 62.2 / 58.9 and
+  //   108.9 / 110.1; of 4 at batch 4, 8 and 16 32.9 / 29.6, 44.6 / 51.4 and
+  //   75.8 / 95.3; of 8 at batch 8 and 16 34.8 / 49.0 and 49.6 / 89.6; of 16
+  //   at batch 16 51.6 / 89.0.
   if (prefix_len > 0 && !(flags & ATTN_PLAN_SHARED_PASS)) {
     attn_decode_plan_t def{};
     st = plan_impl(&d, max_context_len, nullptr, 0, flags, &def);
     if (st != ATTN_OK) return st;
     const int64_t group_rows = (int64_t)prefix_group * d.q_len * (d.num_q_heads / d.num_kv_heads);
     const bool key_streams = def.variant == ATTN_VARIANT_MFMA && def.stage1_waves * 16 > def.rows_per_wg;
-    if (prefix_group == 1 || (key_streams && group_rows < ATTN_SHARED_PASS_MIN_ROWS)) {
+    const bool one_group = prefix_group == d.batch;
+    if (prefix_group == 1 || group_rows < 32 || (one_group && group_rows < 64) ||
+        (key_streams && group_rows < ATTN_SHARED_PASS_MIN_ROWS)) {
       pp.own = def;
       pp.num_splits = def.num_splits;
       pp.workspace_bytes = def.workspace_bytes;

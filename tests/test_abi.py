@@ -351,9 +351,11 @@ def test_prefix_plan_passes_and_split_rule():
 
 def test_prefix_plan_falls_back_where_the_shared_pass_does_not_pay():
     """Without ATTN_PLAN_SHARED_PASS the plan is the default plan over every
-    key for groups of one request, and where the default plan runs four key
-    streams (16-63 rows per KV head) with fewer than SHARED_PASS_MIN_ROWS
-    rows per group; the caller's other flags reach that plan."""
+    key for groups of one request, for fewer than 32 rows per group and KV
+    head, for a single group of fewer than 64, and where the default plan
+    runs four key streams (16-63 rows per KV head) with fewer than
+    SHARED_PASS_MIN_ROWS rows per group; the caller's other flags reach that
+    plan."""
     assert sk.SHARED_PASS_MIN_ROWS == 128
 
     def check_fallback(d, mx, G, prefix, flags=0):
@@ -385,27 +387,34 @@ def test_prefix_plan_falls_back_where_the_shared_pass_does_not_pay():
     # with the private-pages hint the default plan is the one-wave ring: shared
     pv = sk.attn_decode_plan_prefix(d, 68000, 4, 63240, sk.ATTN_PLAN_PRIVATE_PAGES)
     assert pv.prefix_len == 63240
-    # GQA, 8 heads per KV head: the default plan is the one-wave ring, so
-    # every group of two or more shares; a group of one never does
+    # GQA, 8 heads per KV head (the one-wave ring): groups of 2 (16 rows)
+    # fall back; groups of 4 (32 rows) share unless they are the only group;
+    # groups of 8 and 16 share; a group of one never does
     g = desc(B=16)
     assert sk.attn_decode_plan(g, 65536).stage1_waves == 1
-    for G in (2, 4, 8, 16):
-        shared(g, 65536, G, 1024)
     check_fallback(g, 65536, 1, 1024)
+    check_fallback(g, 65536, 2, 1024)
+    for G in (4, 8, 16):
+        shared(g, 65536, G, 1024)
+    g4 = desc(B=4)
+    check_fallback(g4, 65536, 4, 1024)
+    g8 = desc(B=8)
+    shared(g8, 65536, 8, 1024)
     # GQA with 16 heads per KV head (key streams at 16-63 rows): 2 requests
     # (32 rows) fall back, 8 (128 rows) share
     g16 = desc(B=16, Hq=32, Hkv=2)
     check_fallback(g16, 65536, 2, 1024)
     shared(g16, 65536, 8, 1024)
     # draft rows (4 positions x 8 heads = 32 rows at head dim 256: two row
-    # tiles on a ring): groups of two share
+    # tiles on a ring): groups of two (64 rows) share
     dr = desc(B=8, q_len=4, Hq=32, Hkv=4, Dk=256, Dv=256, causal=1)
     shared(dr, 2048, 2, 1024)
     check_fallback(dr, 2048, 1, 1024)
-    # fp32 (vector ALUs): only groups of one fall back
-    f = desc(B=8, Hq=4, Hkv=1, Dk=64, Dv=64, dtype=sk.ATTN_F32)
-    shared(f, 4096, 2, 1024)
-    check_fallback(f, 4096, 1, 1024)
+    # fp32 (vector ALUs), 4 heads per KV head: groups of 8 (32 rows) share,
+    # groups of 4 (16 rows) fall back
+    f = desc(B=16, Hq=4, Hkv=1, Dk=64, Dv=64, dtype=sk.ATTN_F32)
+    shared(f, 4096, 8, 1024)
+    check_fallback(f, 4096, 4, 1024)
     # validation comes first: a prefix too long for the context fails either way
     with pytest.raises(sk.AttnDecodeError):
         sk.attn_decode_plan_prefix(dr, 2048, 1, 2048)

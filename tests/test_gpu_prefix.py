@@ -273,13 +273,14 @@ def test_prefix_full_size_mla_b48_sampled():
     check(d, requests=(0, 9, 47))
 
 
-@pytest.mark.parametrize("name,falls_back", [("mla_b4_g2", True), ("gqa_b3_g1", True), ("gqa_b4_g2", False),
-                                              ("drafts_g3", False), ("mla_b16_p700", False)])
+@pytest.mark.parametrize("name,falls_back", [("mla_b4_g2", True), ("gqa_b3_g1", True), ("gqa_b4_g2", True),
+                                              ("drafts_g3", False), ("mla_b16_p700", False),
+                                              ("mla_wide_b4_g2", False)])
 def test_prefix_fallback_is_the_plain_run(name, falls_back):
     """Without ATTN_PLAN_SHARED_PASS: where the planner keeps the default plan
-    (MLA in groups of 2, groups of one request) attn_decode_run_prefix gives
-    attn_decode_run's bits; elsewhere the shared pass runs and matches the
-    oracle."""
+    (MLA in groups of 2, groups of one request, GQA groups of 16 rows)
+    attn_decode_run_prefix gives attn_decode_run's bits; elsewhere the
+    shared pass runs and matches the oracle."""
     import torch
     inp = inputs(name)
     d = PrefixDecode(inp, flags=0).run()
