@@ -78,7 +78,8 @@ struct MCfg {
   // Again for the lone wave at head dim 128 with one workgroup per CU:
   // 2 / 3 / 4 / 5 tiles, stage 1 18.6 / 15.4 / 15.9 / 16.3 us; and for the
   // drafts' work list of 128-key splits, where 4 tiles put all four blocks
-  // of a workgroup in flight at once: 10.0 against 10.7 us.
+  // of a workgroup in flight at once: 10.0 against 10.7 us; 2 tiles (two
+  // workgroups per CU, 64-key splits) 13.7.
   // The four-wave shape at head dim 128 (prefill, whose keys mostly come
   // from cache) takes 2 tiles, which fits a fourth workgroup per CU: whole
   // op 4 x 2048 132.3 -> 128.0 us, varlen 95.0 -> 90.8.
