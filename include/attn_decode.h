@@ -105,9 +105,10 @@ enum {
                                        streams private pages faster, instead of four key
                                        streams, which compute four blocks at once and pay off
                                        when requests re-read shared prefix pages from the L2;
-                                       and with fewer rows at head dim 128, one one-wave
-                                       workgroup per CU instead of two (two keep the CUs'
-                                       work rate up when the L2 serves shared pages).
+                                       and with fewer rows, one one-wave workgroup per CU
+                                       instead of two at head dim 128 and two instead of four
+                                       at 64 (more keep the CUs' work rate up when the L2
+                                       serves shared pages).
                                        Results do not depend on it (either shape is exact) */
   ATTN_PLAN_SHARED_PASS = 16        /* shared-prefix plans only: run the shared pass where the
                                        planner would take the default plan

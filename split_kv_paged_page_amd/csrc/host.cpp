@@ -384,22 +384,32 @@ attn_status plan_impl(const attn_decode_desc* desc, int32_t max_context_len, con
     p.variant = ATTN_VARIANT_MFMA;
     p.rows_per_wg = 16 * ms.rw;
     p.stage1_waves = ms.rw * ms.kw;
-    // The one-wave ring at head dim 128 holds two 16 KB blocks in flight,
-    // and one such workgroup per CU walked twice the keys at the same rate
-    // with half the partials to merge: 64K GQA whole op 18.73 -> 18.25 us,
-    // and 52.3 -> 51.7 / 99.3 -> 98.0 at batch 4 / 8 (30.2 -> 30.4 at 2).
-    // That holds for one request and for private pages (the hint).  A
-    // batch whose requests may share pages keeps two per CU: once the L2
-    // serves the shared blocks, the wave's own per-block work bounds it.
-    // 64K GQA with 61,440 keys shared (one / two per CU, us per op): batch
-    // 4 in one group 45.8 / 29.5, 8 in one group 84.6 / 49.2, 16 in groups
-    // of 8 161.3 / 89.9; private batches of 4 and 8 unchanged (51.5 / 51.4,
-    // 98.2 / 98.2).
-    // At head dim 64 (8 KB blocks) one per CU was far slower (stage 1 9.96
-    // -> 12.0 us): two keep enough bytes in flight.
-    const bool one_wave_d128 =
-        ms.rw == 1 && ms.kw == 1 && d.head_dim_qk == 128 && (d.batch == 1 || (flags & ATTN_PLAN_PRIVATE_PAGES));
-    wgs_per_cu = kLdsPerCu / ms.smem < 2 || one_wave_d128 ? 1 : 2;
+    // Workgroups per CU: two where the LDS allows, else one; the one-wave
+    // ring (1-15 rows per KV head) depends on the batch.
+    //   * One request, or private pages (the hint): at head dim 128 one per
+    //     CU, whose two 16 KB blocks in flight walk twice the keys at the
+    //     same rate with half the partials to merge (64K GQA whole op
+    //     18.73 -> 18.25 us, batch 4 / 8 52.3 -> 51.7 / 99.3 -> 98.0); at
+    //     head dim 64 (8 KB blocks) two, one being far slower (stage 1 9.96
+    //     -> 12.0 us).
+    //   * A batch whose requests may share pages: two at head dim 128 and
+    //     four at 64.  Once the L2 serves the shared blocks, each wave's own
+    //     per-block work bounds the batch, and more waves per CU share it.
+    //     61,440 of 65,536 keys shared (us per op): head dim 128, one / two
+    //     per CU, batch 4 in one group 45.8 / 29.5, 8 in one group 84.6 /
+    //     49.2, 16 in groups of 8 161.3 / 89.9; head dim 64, two / four,
+    //     23.2 / 19.2, 39.3 / 28.6, 71.7 / 49.1.  On private pages planned
+    //     without the hint the same choice costs at most 2%: head dim 128
+    //     batch 2 / 4 / 8 30.4 / 51.3 / 97.4 against 30.1 / 51.7 / 99.4;
+    //     head dim 64 18.2 / 29.9 / 52.0 against 18.5 / 30.0 / 52.1.
+    const bool lone = ms.rw == 1 && ms.kw == 1;
+    const bool may_share = d.batch > 1 && !(flags & ATTN_PLAN_PRIVATE_PAGES);
+    if (lone && d.head_dim_qk == 128)
+      wgs_per_cu = may_share ? 2 : 1;
+    else if (lone && d.head_dim_qk == 64 && may_share)
+      wgs_per_cu = 4;
+    else
+      wgs_per_cu = kLdsPerCu / ms.smem < 2 ? 1 : 2;
   } else {
     const int rt = pick_rows_per_wg(d.dtype, d.head_dim_qk, d.head_dim_v, rows);
     if (!rt)
@@ -426,11 +436,11 @@ attn_status plan_impl(const attn_decode_desc* desc, int32_t max_context_len, con
     S = kNumCu / d.batch;
     if (S < 1) S = 1;
   } else {
-    // One full round of workgroups: two per CU where the LDS allows it (VALU
-    // workgroups, the lone MFMA wave at head dim 64), else one (and one for
-    // the lone wave at head dim 128, above).  Three lone waves per CU at head
-    // dim 128 were slower still (64K GQA stage 1: 16.3 us against 15.7 at
-    // two, 15.3 at one).
+    // One full round of workgroups at the workgroups per CU chosen above
+    // (two where the LDS allows, one or two for the lone wave at head dim
+    // 128 and two or four at 64).  Three lone waves per CU at head dim 128
+    // were slower still for one request (64K GQA stage 1: 16.3 us against
+    // 15.7 at two, 15.3 at one).
     const int per_split = d.batch * d.num_kv_heads * p.head_tiles;
     const int target = wgs_per_cu * kNumCu;
     S = target / per_split;

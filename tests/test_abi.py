@@ -122,7 +122,7 @@ def test_default_policy_fills_the_chip():
 def test_workgroups_per_cu_of_the_one_wave_ring():
     """The one-wave ring at head dim 128 runs one workgroup per CU for one
     request or a batch with the private-pages hint, and two for a batch whose
-    requests may share pages; at head dim 64 always two."""
+    requests may share pages; at head dim 64 two, and four for such a batch."""
     priv = sk.ATTN_PLAN_PRIVATE_PAGES
     S = lambda d, f=0: sk.attn_decode_plan(d, 65536, 0, f).num_splits
     assert S(desc(B=1)) == 128 and S(desc(B=1), priv) == 128          # 256 / (1 x 2 KV heads)
@@ -130,6 +130,7 @@ def test_workgroups_per_cu_of_the_one_wave_ring():
     assert S(desc(B=8)) == 32 and S(desc(B=8), priv) == 16
     d64 = dict(Dk=64, Dv=64)
     assert S(desc(B=1, **d64)) == 256 and S(desc(B=4, **d64), priv) == 64
+    assert S(desc(B=4, **d64)) == 128 and S(desc(B=8, **d64)) == 64     # 1024 / (B x 2)
 
 
 def test_kernel_choice_by_rows_per_kv_head():
