@@ -16,13 +16,14 @@ roofline entry.
 Prints one JSON line.  value = logical KV bytes per op / time per op (GB/s)
 of the headline workload (--config, 64K GQA by default).  The default run
 also times the other decode workloads (--extra): the tiny fp32 check, MLA
-batch 48 with and without shared prefixes, the 128-head MLA and the varlen
-drafts, each under "configs" with its whole-op and stage-1 times, its own
+batch 48 with and without shared prefixes, one MLA request, the 128-head MLA,
+the varlen drafts and 8 GQA requests sharing a 61,440-key prefix, each under
+"configs" with its whole-op and stage-1 times, its own
 stage-1 roofline entry, a plain cold read of the same KV bytes (unique bytes
 where prefixes are shared) and, for shared prefixes, the unique-bytes rate.
-"mla_b48+prefix" is MLA batch 48 again through the shared-prefix plan
-(attn_decode_plan_prefix: each group's shared keys scored once for all its
-members' rows), whole op only; --prefix times only that for --config.
+A name ending in "+prefix" is that workload again through the shared-prefix
+plan (attn_decode_plan_prefix: each group's shared keys scored once for all
+its members' rows), whole op only; --prefix times only that for --config.
 
 Beside stage 1 the line carries a plain device-memory read timed the same
 way (libsplitkv_probe.so): a 2 GiB streaming read, the part's practical read
@@ -258,7 +259,7 @@ def cpu_baseline(inp, kv_bytes, budget_s):
 # Configurations timed beside the headline one in the default run, each with
 # its own stage-1 roofline: the tiny fp32 check, MLA batch 48 with and
 # without shared prefixes, the 128-head MLA and the varlen drafts.
-EXTRA_CONFIGS = "gqa_tiny_f32,mla_b48,mla_b48+prefix,mla_b48_ctl,mla_b1,mla_wide,varlen_drafts"
+EXTRA_CONFIGS = "gqa_tiny_f32,mla_b48,mla_b48+prefix,mla_b48_ctl,mla_b1,mla_wide,varlen_drafts,gqa_64k_b8_shared,gqa_64k_b8_shared+prefix"
 PREFIX_SUFFIX = "+prefix"   # an --extra entry <workload>+prefix: that workload through the shared-prefix plan
 
 

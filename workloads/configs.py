@@ -22,6 +22,9 @@ Workloads that stand in for the traffic the pages measure:
   32 query heads over 4 KV heads, head dim 256, page size 16.  The context
   lengths are the varlen sweep of rocm-libraries PR #10102 (Technical
   Details, launcher-cache paragraph).
+* ``gqa_64k_b8_shared`` - 8 requests of the 64K GQA shape that share their
+  first 61,440 keys (one group; prefix caching on GQA, the GQA counterpart
+  of the MLA batch-48 sharing).
 * ``gqa_64k_d64``    - the 64K GQA shape at head dim 64, bf16: the head dim
   whose 128-byte K rows rocm-libraries PR #10102 pads in LDS (Motivation
   bank table).
@@ -162,6 +165,10 @@ def _mk() -> dict:
             name=f"prefill_varlen_d{d}", batch=6, q_len=2048, num_q_heads=16, num_kv_heads=4,
             head_dim_qk=d, head_dim_v=d, page_size=16, kv_dtype="bf16",
             context_lens=(256, 512, 768, 1024, 1536, 2048), pool_pages=768, causal=True, seed=8)
+    c["gqa_64k_b8_shared"] = Workload(
+        name="gqa_64k_b8_shared", batch=8, q_len=1, num_q_heads=16, num_kv_heads=2,
+        head_dim_qk=128, head_dim_v=128, page_size=16, kv_dtype="bf16",
+        context_lens=(65536,) * 8, pool_pages=3840 + 8 * 256, seed=9, prefix_group=8, prefix_len=61440)
     c["gqa_64k_d64"] = Workload(
         name="gqa_64k_d64", batch=1, q_len=1, num_q_heads=16, num_kv_heads=2,
         head_dim_qk=64, head_dim_v=64, page_size=16, kv_dtype="bf16",
