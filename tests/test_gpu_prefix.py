@@ -304,6 +304,30 @@ def test_prefix_fallback_is_the_plain_run(name, falls_back):
     assert torch.equal(d.lse.view(torch.int32), lse.view(torch.int32))
 
 
+def test_prefix_full_size_gqa_b8_shared_sampled():
+    """Eight 64K-key GQA requests sharing 61,440 keys: the shared-prefix plan
+    (which the planner takes for this group) and the default plan (two
+    one-wave workgroups per CU), sampled requests against the oracle."""
+    import torch
+    inp = generate(get("gqa_64k_b8_shared"))
+    d = PrefixDecode(inp, flags=0).run()
+    say(f"prefix gqa_64k_b8_shared S = {d.Sp} + {d.So}")
+    assert d.prefix == 61440 and d.Sp > 0
+    check(d, requests=(0, 5))
+    t = d.t
+    plan = sk.attn_decode_plan(d.desc, 65536)
+    ws = torch.empty(plan.workspace_bytes // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(d.out)
+    lse = torch.empty_like(d.lse)
+    sk.attn_decode_run(plan, t["q"], t["k_cache"], t["v_cache"], t["page_table"], t["context_lens"],
+                       float(inp.scale), 0, out, lse, ws)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_reference(inp, requests=(0, 5))
+    sel = [0, 5]
+    assert row_rel_err(out.double().cpu().numpy()[sel], ro[sel]) <= tol_for(inp.w)
+    assert lse_err(lse.double().cpu().numpy()[sel], rl[sel]) <= 1e-3
+
+
 @pytest.mark.parametrize("name", ["mla_b16_p700", "gqa_b4_g2"])
 def test_prefix_graph_replays_match_eager(name):
     """attn_decode_run_prefix allocates nothing and never synchronises: its
